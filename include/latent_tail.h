@@ -1,0 +1,149 @@
+/*
+ * latent_tail.h -- C ABI of liblatenttail.so: the latent-MoE output tail on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages this library follows):
+ *   [PR51253]  prhub report of vLLM PR #51253, "[ROCm][Perf] Kimi-K3 Shard
+ *              Latent MoE up-projection for ROCm path".
+ *   [PR50383]  prhub report of vLLM PR #50383 (tiered tail of the K3
+ *              latent-MoE runner; column-parallel `_shard_up_proj_tail`).
+ *   [PR50593]  prhub report of vLLM PR #50593, "[Kimi-K3][AMD] Fuse AttnRes
+ *              state updates and norms" (bf16 storage round trip, fp32 norm
+ *              variance, token-count launch heuristic, HIP graph replay).
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as pointers to their 16-bit patterns.
+ *   - Every pointer is a DEVICE pointer on the current HIP device, owned by
+ *     the caller; the library keeps no pointer after a call returns.
+ *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *     NULL means the default stream).  No call synchronises the device or
+ *     copies between host and device, except that growing the internal
+ *     scratch buffer (see lt_reserve) synchronises `stream` first.
+ *   - Argument errors are reported before anything is launched; in that case
+ *     no device memory has been read or written.
+ *   - The library is thread-safe.  Results are bit-identical from run to run
+ *     for the same arguments (no atomics, fixed reduction order).
+ */
+#ifndef LATENT_TAIL_H
+#define LATENT_TAIL_H
+
+#include <stdint.h>
+
+#if defined(LT_BUILDING_LIBRARY)
+#define LT_API __attribute__((visibility("default")))
+#else
+#define LT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define LT_OK 0
+#define LT_ERR_INVALID_ARG 1   /* an argument is out of range, NULL or overlaps */
+#define LT_ERR_UNSUPPORTED 2   /* legal in principle, outside what this build handles */
+#define LT_ERR_NO_MEMORY 3     /* scratch could not be (re)allocated */
+#define LT_ERR_HIP 4           /* a HIP call or kernel launch failed */
+
+/* Largest latent width the kernels accept (the model's is 1024). */
+#define LT_MAX_L 2048
+
+/*
+ * lt_latent_tail -- one GPU's share of the latent-MoE output tail.
+ *
+ * Defined by [PR50383 Key source snippets, `_shard_up_proj_tail`] and the
+ * expected value of [PR51253 Key source snippets, `_check_matches_replicated`],
+ * on one GPU: the tensor-parallel all-reduce of the routed latent becomes a
+ * local sum over `n_partials` partials, and the final all-reduce that stitches
+ * the column shards is left to the caller.  For t < T and 0 <= j < n:
+ *
+ *   s[t,k]  = bf16( sum_p partials[p][t][k] )               (fp32 sum)
+ *   y[t,k]  = bf16( s[t,k] * rsqrt(mean_k s[t,k]^2 + eps) * norm_w[k] )
+ *             (fp32 variance and scaling; y = s when norm_w == NULL)
+ *   out[t][c0+j] = bf16( out[t][c0+j] + sum_k y[t,k] * W[c0+j][k] )
+ *             (fp32 accumulation, one rounding: the beta-add of `addmm_`)
+ *
+ * Every other element of `out` -- columns outside [c0, c0+n), the padding
+ * between H and ld_out, rows >= T -- is left bit-identical
+ * ([PR51253 Key source snippets, `_check_writes_only_its_own_shard`]).
+ * alpha is 1: the pages require a routed scaling factor of 1
+ * ([PR51253 Implementation, item 2]).
+ *
+ * Arguments:
+ *   partials    [n_partials][T][L] bf16, packed contiguous; 16-byte aligned.
+ *   n_partials  >= 1.
+ *   T           tokens, >= 0.
+ *   L           latent width, 8 <= L <= LT_MAX_L, L % 8 == 0.
+ *   norm_w      [L] bf16 RMSNorm weight, 16-byte aligned, or NULL to skip
+ *               the norm ([PR50383 Key source snippets]: the norm is optional).
+ *   eps         >= 0 and finite; added to the mean square inside the root.
+ *   W           [H][L] bf16 row-major: the full replicated up-projection
+ *               weight (rows = hidden index); 16-byte aligned.
+ *   H           hidden width = rows of W = logical columns of out, >= 1.
+ *   c0, n       column window: 0 <= c0, 0 <= n, c0 + n <= H.  Any window is
+ *               legal (no divisibility requirement).
+ *   out         [T][ld_out] bf16 shared-expert partial, updated in place on
+ *               the window only; 2-byte aligned.  Must not overlap
+ *               partials, norm_w or W.
+ *   ld_out      row stride of out in elements, ld_out >= H.
+ *   stream      hipStream_t (NULL = default stream).
+ *
+ * Returns LT_OK, LT_ERR_INVALID_ARG (NULL pointer where data is needed,
+ * out-of-range size or window, non-finite or negative eps, out overlapping an
+ * input), LT_ERR_UNSUPPORTED (L outside 8..LT_MAX_L or not a multiple of 8, a
+ * misaligned pointer), LT_ERR_NO_MEMORY (the scratch of the T > skinny path
+ * could not grow, or would have to grow while `stream` is being captured into
+ * a graph), or LT_ERR_HIP.  T == 0 or n == 0 returns LT_OK with nothing
+ * launched ([PR50383 Key source snippets]: an empty batch is a legal state).
+ */
+LT_API int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
+                   const void *norm_w, float eps, const void *W, int64_t H,
+                   int64_t c0, int64_t n, void *out, int64_t ld_out, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+LT_API const char *lt_status_string(int status);
+
+/*
+ * lt_reserve -- pre-size the library-owned scratch used by calls with
+ * T > skinny_max on `stream` of the current device: a [max_T][L] bf16 latent
+ * buffer.  Calls that then fit never allocate, so they can be captured into a
+ * HIP graph ([PR50593 Implementation, item 4]: graph capture and replay at
+ * varying shapes is part of the validation there).  The buffer belongs to
+ * (device, stream) and lives until lt_release_scratch or process exit.
+ * Returns LT_OK, LT_ERR_INVALID_ARG, LT_ERR_NO_MEMORY or LT_ERR_HIP.
+ * Synchronises `stream` when it has to grow the buffer.
+ */
+LT_API int lt_reserve(int64_t max_T, int64_t L, void *stream);
+
+/* Free every scratch buffer of the current device (synchronises the device). */
+LT_API int lt_release_scratch(void);
+
+/*
+ * lt_set_skinny_max_tokens -- the token-count dispatcher's threshold
+ * ([PR50383 Implementation, item 1]: the tail variant is chosen from the token
+ * count alone).  Calls with T <= t take the weight-streaming path, the others
+ * the sum+RMSNorm kernel followed by the MFMA GEMM.  t < 0 restores the
+ * default (64, or the environment variable LT_SKINNY_MAX_T if set).  Returns
+ * the previous threshold.  Process-wide.
+ */
+LT_API int64_t lt_set_skinny_max_tokens(int64_t t);
+
+/* Current threshold (see lt_set_skinny_max_tokens). */
+LT_API int64_t lt_get_skinny_max_tokens(void);
+
+/*
+ * lt_path_for -- which path a call with these sizes takes:
+ * 0 = nothing launched (T == 0 or n == 0), 1 = weight-streaming (skinny),
+ * 2 = sum+RMSNorm kernel then MFMA GEMM.  Host-only, launches nothing.
+ */
+LT_API int lt_path_for(int64_t T, int64_t n);
+
+/* Library version string, e.g. "liblatenttail 0.1.0 gfx950". */
+LT_API const char *lt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENT_TAIL_H */

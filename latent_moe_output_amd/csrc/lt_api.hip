@@ -1,0 +1,230 @@
+// lt_api.hip -- C ABI of liblatenttail.so: validation, scratch, dispatch.
+//
+// The entry point follows [PR50383 Key source snippets, `_shard_up_proj_tail`]
+// on one GPU: reduce the routed partials (locally, over n_partials), norm,
+// narrow W rows and out columns to [c0, c0+n), add the projection in place.
+// The token-count dispatcher mirrors the tier choice of [PR50383
+// Implementation, item 1], reduced to the two single-GPU paths:
+//   T <= skinny_max  -> one weight-streaming launch per 64 tokens (k_skinny)
+//   T >  skinny_max  -> k_sum_rmsnorm into a scratch latent, then k_gemm.
+// The pages' own fallback is silent ([PR51253 Implementation, item 2]); a
+// library cannot fall back to a path it does not own, so every violated
+// precondition is an explicit status code returned before any launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "latent_tail.h"
+#include "lt_internal.h"
+
+namespace {
+
+constexpr int64_t kDefaultSkinnyMax = 64;
+
+std::atomic<int64_t> g_skinny_max{-1};
+
+int64_t default_skinny_max()
+{
+    static const int64_t v = [] {
+        const char *e = std::getenv("LT_SKINNY_MAX_T");
+        if (e && *e) {
+            char *end = nullptr;
+            long long x = std::strtoll(e, &end, 10);
+            if (end && *end == '\0' && x >= 0) return (int64_t)x;
+        }
+        return kDefaultSkinnyMax;
+    }();
+    return v;
+}
+
+int64_t skinny_max()
+{
+    int64_t v = g_skinny_max.load(std::memory_order_relaxed);
+    return v < 0 ? default_skinny_max() : v;
+}
+
+// ---- scratch: one [T][L] bf16 latent buffer per (device, stream) ----------
+struct Scratch {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, uintptr_t>, Scratch> g_scratch;
+
+int ensure_scratch(size_t bytes, hipStream_t stream, void **out_ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LT_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    Scratch &s = g_scratch[{dev, reinterpret_cast<uintptr_t>(stream)}];
+    if (s.bytes >= bytes) {
+        *out_ptr = s.ptr;
+        return LT_OK;
+    }
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return LT_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return LT_ERR_NO_MEMORY;  // never allocate in capture
+    // Work already queued on this stream may still read the old buffer.
+    if (s.ptr) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return LT_ERR_HIP;
+        if (hipFree(s.ptr) != hipSuccess) return LT_ERR_HIP;
+        s.ptr = nullptr;
+        s.bytes = 0;
+    }
+    size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
+    void *p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) {
+        (void)hipGetLastError();
+        return LT_ERR_NO_MEMORY;
+    }
+    s.ptr = p;
+    s.bytes = want;
+    *out_ptr = p;
+    return LT_OK;
+}
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *r = a * b;
+    return true;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *lt_status_string(int status)
+{
+    switch (status) {
+    case LT_OK: return "LT_OK";
+    case LT_ERR_INVALID_ARG: return "LT_ERR_INVALID_ARG: argument out of range, NULL or overlapping";
+    case LT_ERR_UNSUPPORTED: return "LT_ERR_UNSUPPORTED: latent width or alignment not handled";
+    case LT_ERR_NO_MEMORY: return "LT_ERR_NO_MEMORY: scratch could not be allocated";
+    case LT_ERR_HIP: return "LT_ERR_HIP: HIP call or kernel launch failed";
+    default: return "unknown lt status";
+    }
+}
+
+const char *lt_version(void) { return "liblatenttail 0.1.0 gfx950"; }
+
+int64_t lt_set_skinny_max_tokens(int64_t t)
+{
+    const int64_t prev = skinny_max();
+    g_skinny_max.store(t < 0 ? -1 : t, std::memory_order_relaxed);
+    return prev;
+}
+
+int64_t lt_get_skinny_max_tokens(void) { return skinny_max(); }
+
+int lt_path_for(int64_t T, int64_t n)
+{
+    if (T <= 0 || n <= 0) return 0;
+    return T <= skinny_max() ? 1 : 2;
+}
+
+int lt_reserve(int64_t max_T, int64_t L, void *stream)
+{
+    if (max_T < 0 || L < 1) return LT_ERR_INVALID_ARG;
+    int64_t elems = 0;
+    if (!mul_ok(max_T, L, &elems) || elems > INT64_MAX / 2) return LT_ERR_INVALID_ARG;
+    if (elems == 0) return LT_OK;
+    void *p = nullptr;
+    return ensure_scratch((size_t)elems * 2, reinterpret_cast<hipStream_t>(stream), &p);
+}
+
+int lt_release_scratch(void)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LT_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (hipDeviceSynchronize() != hipSuccess) return LT_ERR_HIP;
+    for (auto it = g_scratch.begin(); it != g_scratch.end();) {
+        if (it->first.first == dev) {
+            if (it->second.ptr && hipFree(it->second.ptr) != hipSuccess) return LT_ERR_HIP;
+            it = g_scratch.erase(it);
+        } else {
+            ++it;
+        }
+    }
+    return LT_OK;
+}
+
+int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
+                   const void *norm_w, float eps, const void *W, int64_t H, int64_t c0,
+                   int64_t n, void *out, int64_t ld_out, void *stream)
+{
+    // ---- sizes and window
+    if (n_partials < 1 || T < 0 || L < 1 || H < 1 || c0 < 0 || n < 0 || c0 > H || n > H - c0 ||
+        ld_out < H)
+        return LT_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.f) return LT_ERR_INVALID_ARG;
+    if (L % 8 != 0 || L > LT_MAX_L) return LT_ERR_UNSUPPORTED;
+    if (T == 0 || n == 0) return LT_OK;
+    if (!partials || !W || !out) return LT_ERR_INVALID_ARG;
+
+    int64_t tl = 0, ptl = 0, hl = 0, tld = 0;
+    if (!mul_ok(T, L, &tl) || !mul_ok(tl, n_partials, &ptl) || !mul_ok(H, L, &hl) ||
+        !mul_ok(T - 1, ld_out, &tld) || tld > INT64_MAX - H || ptl > INT64_MAX / 2 ||
+        hl > INT64_MAX / 2 || tld + H > INT64_MAX / 2)
+        return LT_ERR_INVALID_ARG;
+    if (n > 0x7FFFFFFF || L > 0x7FFFFFFF) return LT_ERR_UNSUPPORTED;
+
+    // ---- alignment (16-byte vector loads of every input row)
+    if (!aligned(partials, 16) || !aligned(W, 16) || (norm_w && !aligned(norm_w, 16)) ||
+        !aligned(out, 2))
+        return LT_ERR_UNSUPPORTED;
+
+    // ---- out must not alias an input
+    const size_t out_bytes = (size_t)(tld + H) * 2;
+    if (ranges_overlap(out, out_bytes, partials, (size_t)ptl * 2) ||
+        ranges_overlap(out, out_bytes, W, (size_t)hl * 2) ||
+        ranges_overlap(out, out_bytes, norm_w, (size_t)L * 2))
+        return LT_ERR_INVALID_ARG;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const uint16_t *part = static_cast<const uint16_t *>(partials);
+    const uint16_t *nw = static_cast<const uint16_t *>(norm_w);
+    const uint16_t *Wn = static_cast<const uint16_t *>(W) + c0 * L;
+    uint16_t *outn = static_cast<uint16_t *>(out) + c0;
+
+    (void)hipGetLastError();  // start from a clean error state
+    if (T <= skinny_max()) {
+        const int per = lt::skinny_tokens_per_launch((int)L);
+        for (int64_t tb = 0; tb < T; tb += per) {
+            const int tc = (int)((T - tb) < per ? (T - tb) : per);
+            hipError_t e = lt::launch_skinny(part + tb * L, tl, n_partials, tc, (int)L, nw, eps,
+                                             Wn, (int)n, outn + tb * ld_out, ld_out, s);
+            if (e != hipSuccess) return LT_ERR_HIP;
+        }
+        return LT_OK;
+    }
+
+    void *scratch = nullptr;
+    int st = ensure_scratch((size_t)tl * 2, s, &scratch);
+    if (st != LT_OK) return st;
+    uint16_t *y = static_cast<uint16_t *>(scratch);
+    if (lt::launch_sum_rmsnorm(part, tl, n_partials, T, (int)L, nw, eps, y, s) != hipSuccess)
+        return LT_ERR_HIP;
+    if (lt::launch_gemm(y, T, (int)L, Wn, (int)n, outn, ld_out, s) != hipSuccess)
+        return LT_ERR_HIP;
+    return LT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// lt_internal.h -- launchers of the tail's kernels (library-internal).
+//
+// Every launcher takes device pointers that the C-ABI layer has already
+// validated (sizes, alignment, window), so the kernels can rely on:
+//   L % 8 == 0, 8 <= L <= LT_MAX_L; rows of partials / latent / W 16-byte
+//   aligned; T, n >= 1; outn = out + c0 with row stride ld_out.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lt {
+
+// Weight-streaming path: fused partial sum + RMSNorm + projection +
+// beta-add for tokens [0, T) of `part` (T <= 64; partial stride `pstride`).
+hipError_t launch_skinny(const uint16_t *part, int64_t pstride, int P, int T, int L,
+                         const uint16_t *norm_w, float eps, const uint16_t *Wn, int n,
+                         uint16_t *outn, int64_t ld_out, hipStream_t stream);
+
+// Largest token count one skinny launch handles for latent width L.
+int skinny_tokens_per_launch(int L);
+
+// Partial sum + RMSNorm into a packed [T][L] bf16 latent.
+hipError_t launch_sum_rmsnorm(const uint16_t *part, int64_t pstride, int P, int64_t T,
+                              int L, const uint16_t *norm_w, float eps, uint16_t *y,
+                              hipStream_t stream);
+
+// out[t][j] = bf16(out[t][j] + sum_k y[t][k] * Wn[j][k]) for t < T, j < n.
+hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
+                       uint16_t *outn, int64_t ld_out, hipStream_t stream);
+
+}  // namespace lt

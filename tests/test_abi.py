@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The shared library must load, export every function declared in
+include/*.h, and reject bad arguments before touching the GPU.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import re
+
+import pytest
+
+from latent_moe_output_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"LT_API\s+[\w\s\*]*?\b(lt_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for must in ("lt_latent_tail", "lt_status_string", "lt_reserve", "lt_set_skinny_max_tokens"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_the_c_abi_is_exported():
+    import subprocess
+
+    res = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         capture_output=True, text=True, check=True)
+    text_syms = [ln.split()[-1] for ln in res.stdout.splitlines() if " T " in ln]
+    assert sorted(text_syms) == _declared_functions()
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in binding.lt_version()
+    for code in range(5):
+        assert binding.lt_status_string(code).startswith("LT_")
+    assert binding.lt_status_string(99) == "unknown lt status"
+
+
+def test_dispatcher_threshold(lib):
+    prev = binding.lt_set_skinny_max_tokens(-1)
+    try:
+        assert binding.lt_get_skinny_max_tokens() == 64
+        assert binding.lt_path_for(0, 7168) == 0
+        assert binding.lt_path_for(5, 0) == 0
+        assert binding.lt_path_for(64, 7168) == 1
+        assert binding.lt_path_for(65, 7168) == 2
+        assert binding.lt_set_skinny_max_tokens(0) == 64
+        assert binding.lt_path_for(1, 7168) == 2
+        binding.lt_set_skinny_max_tokens(1 << 20)
+        assert binding.lt_path_for(8192, 7168) == 1
+    finally:
+        binding.lt_set_skinny_max_tokens(-1 if prev == 64 else prev)
+
+
+FAKE = 1 << 32   # a 16-byte-aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_partials=0), binding.LT_ERR_INVALID_ARG),
+    (dict(T=-1), binding.LT_ERR_INVALID_ARG),
+    (dict(L=0), binding.LT_ERR_INVALID_ARG),
+    (dict(H=0), binding.LT_ERR_INVALID_ARG),
+    (dict(c0=-1), binding.LT_ERR_INVALID_ARG),
+    (dict(n=-1), binding.LT_ERR_INVALID_ARG),
+    (dict(c0=7000, n=200), binding.LT_ERR_INVALID_ARG),
+    (dict(ld_out=7167), binding.LT_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), binding.LT_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), binding.LT_ERR_INVALID_ARG),
+    (dict(eps=-1e-6), binding.LT_ERR_INVALID_ARG),
+    (dict(partials=None), binding.LT_ERR_INVALID_ARG),
+    (dict(W=None), binding.LT_ERR_INVALID_ARG),
+    (dict(out=None), binding.LT_ERR_INVALID_ARG),
+    (dict(L=1020), binding.LT_ERR_UNSUPPORTED),
+    (dict(L=4096), binding.LT_ERR_UNSUPPORTED),
+    (dict(partials=FAKE + 8), binding.LT_ERR_UNSUPPORTED),
+    (dict(W=FAKE + 2), binding.LT_ERR_UNSUPPORTED),
+    (dict(norm_w=FAKE + 4), binding.LT_ERR_UNSUPPORTED),
+    (dict(out=FAKE + 1), binding.LT_ERR_UNSUPPORTED),
+    (dict(out=FAKE), binding.LT_ERR_INVALID_ARG),            # out == partials
+    (dict(out=FAKE + (1 << 20)), binding.LT_ERR_INVALID_ARG),  # out inside W
+])
+def test_invalid_arguments_are_rejected_before_launch(lib, kw, code):
+    args = dict(partials=FAKE, n_partials=1, T=16, L=1024, norm_w=FAKE + (1 << 30), eps=1e-6,
+                W=FAKE + (1 << 20), H=7168, c0=0, n=7168, out=FAKE + (1 << 31), ld_out=7168)
+    args.update(kw)
+    assert binding.lt_latent_tail(**args) == code
+
+
+def test_empty_calls_return_ok_without_launch(lib):
+    args = dict(partials=FAKE, n_partials=1, T=16, L=1024, norm_w=None, eps=1e-6,
+                W=FAKE + (1 << 20), H=7168, c0=0, n=7168, out=FAKE + (1 << 31), ld_out=7168)
+    assert binding.lt_latent_tail(**dict(args, T=0)) == binding.LT_OK
+    assert binding.lt_latent_tail(**dict(args, n=0)) == binding.LT_OK
+    assert binding.lt_latent_tail(**dict(args, T=0, partials=None, W=None, out=None)) == binding.LT_OK
+
+
+def test_reserve_rejects_bad_sizes(lib):
+    assert binding.lt_reserve(-1, 1024) == binding.LT_ERR_INVALID_ARG
+    assert binding.lt_reserve(4, 0) == binding.LT_ERR_INVALID_ARG
+    assert binding.lt_reserve(0, 1024) == binding.LT_OK

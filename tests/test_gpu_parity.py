@@ -1,0 +1,393 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: |gpu - oracle| <= 3e-2 + 1.6e-2 * |oracle| on every window element,
+and bit-identical everywhere else; bit-exact where the arithmetic is exact
+(dyadic inputs, identity projections, split partials, shards).
+
+Workloads are the seeded recipes of latent_moe_output_amd.synth.  Sizes
+the oracle finishes in seconds are compared element by element; the full
+prefill / ragged sizes (launched exactly as the benchmark launches them) are
+compared on sampled rows -- every column of those rows -- plus the untouched
+region over the whole buffer.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gpu_util import DevInputs, assert_window_close, dev, eps32, host, sample_rows, say
+from latent_moe_output_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    binding.load()
+    prev = binding.lt_set_skinny_max_tokens(-1)
+    yield
+    binding.lt_set_skinny_max_tokens(-1 if prev == 64 else prev)
+
+
+@pytest.fixture()
+def forced():
+    """Force the dispatcher threshold for one test, restoring the default."""
+    def _set(t):
+        binding.lt_set_skinny_max_tokens(t)
+    yield _set
+    binding.lt_set_skinny_max_tokens(-1)
+
+
+def _sync():
+    import torch
+
+    torch.cuda.synchronize()
+
+
+def _run_full(wl, seed=0, **kw):
+    """GPU result and oracle result for the whole buffer."""
+    from oracle import oracle
+
+    d = synth.generate(wl, seed=seed)
+    di = DevInputs(d)
+    say("case %s T=%d L=%d H=%d P=%d c0=%d n=%d ld=%d norm=%s seed=%d path=%d" % (
+        wl.name, wl.T, wl.L, wl.H, wl.P, wl.c0, wl.n, wl.ld_out, wl.norm, seed,
+        binding.lt_path_for(wl.T, wl.n)))
+    binding.check(di.call(wl, **kw))
+    _sync()
+    got = host(di.out)
+    ref = oracle.latent_tail(d["partials"], d["norm_w"], eps32(wl), d["W"], wl.c0, wl.n, d["out"])
+    return d, got, ref
+
+
+# --------------------------------------------------------------------------
+# the configured workloads
+# --------------------------------------------------------------------------
+
+def test_tiny_workload():
+    wl = synth.WORKLOADS["tiny"]
+    _, got, ref = _run_full(wl)
+    assert_window_close(got, ref, wl.c0, wl.n, "tiny")
+
+
+@pytest.mark.parametrize("T", synth.DECODE_TOKENS)
+def test_decode_workload(T):
+    wl = synth.WORKLOADS["decode"].with_T(T)
+    _, got, ref = _run_full(wl)
+    assert_window_close(got, ref, wl.c0, wl.n, "decode T=%d" % T)
+
+
+def test_shard_workload():
+    wl = synth.WORKLOADS["shard"]
+    _, got, ref = _run_full(wl)
+    assert_window_close(got, ref, wl.c0, wl.n, "shard")
+
+
+@pytest.mark.parametrize("name", ["prefill", "ragged", "ragged_nonorm"])
+def test_large_workload_sampled(name):
+    """Full-size call; oracle on sampled rows (all columns); untouched
+    elements checked over the whole buffer."""
+    from oracle import oracle
+
+    wl = synth.WORKLOADS[name]
+    d = synth.generate(wl, seed=0)
+    di = DevInputs(d)
+    say("case %s (full size, sampled rows)" % name)
+    binding.check(di.call(wl))
+    _sync()
+    got = host(di.out)
+    rows = sample_rows(wl.T, k=48, seed=1)
+    ref = oracle.latent_tail(d["partials"][:, rows, :], d["norm_w"], eps32(wl), d["W"], wl.c0,
+                             wl.n, d["out"][rows])
+    assert_window_close(got[rows], ref, wl.c0, wl.n, name)
+    outside = np.ones(got.shape, dtype=bool)
+    outside[:, wl.c0:wl.c0 + wl.n] = False
+    assert np.array_equal(got[outside], d["out"][outside])
+
+
+# --------------------------------------------------------------------------
+# dispatch boundary and forced paths
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [63, 64, 65, 100])
+@pytest.mark.parametrize("thr", [0, 1000, -1])
+def test_dispatch_boundary_both_paths(T, thr, forced):
+    forced(thr)
+    wl = synth.Workload("boundary", T=T, L=1024, H=1536, P=2, c0=320, n=800, ld_out=1544,
+                        part_std=0.7)
+    _, got, ref = _run_full(wl, seed=T)
+    assert_window_close(got, ref, wl.c0, wl.n, "T=%d thr=%d" % (T, thr))
+
+
+def test_paths_give_identical_latents(forced):
+    """With W = I (H = L) and out = 0 the output is the latent itself; the
+    weight-streaming and GEMM paths must produce the same bits, and those
+    bits must be the oracle's latent within tolerance."""
+    from oracle import oracle
+
+    L, T = 1024, 48
+    rng = np.random.Generator(np.random.PCG64(3))
+    parts = synth.to_bf16_bits(rng.standard_normal((3, T, L)) * 0.6)
+    nw = synth.to_bf16_bits(1 + 0.1 * rng.standard_normal(L))
+    eye = synth.to_bf16_bits(np.eye(L))
+    outs = []
+    for thr in (1000, 0):
+        forced(thr)
+        d = dict(partials=parts, norm_w=nw, W=eye, out=np.zeros((T, L), np.uint16))
+        di = DevInputs(d)
+        wl = synth.Workload("eye", T=T, L=L, H=L, P=3, c0=0, n=L, ld_out=L)
+        say("identity latent thr=%d" % thr)
+        binding.check(di.call(wl))
+        _sync()
+        outs.append(host(di.out))
+    assert np.array_equal(outs[0], outs[1])
+    y = oracle.latent(parts, nw, eps32(synth.WORKLOADS["tiny"]))
+    assert_window_close(outs[0], y, 0, L, "identity latent")
+
+
+# --------------------------------------------------------------------------
+# exact cases: bit-exact against the oracle
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [5, 200])
+def test_dyadic_inputs_are_bit_exact(T):
+    """Norm off, small-integer latent, W in {-2..2}/16: every partial sum and
+    projection is exact in fp32, so only the final rounding remains and the
+    GPU must equal the oracle bit for bit."""
+    from oracle import oracle
+
+    rng = np.random.Generator(np.random.PCG64(4))
+    L, H = 1024, 640
+    A = rng.integers(-2, 3, (2, T, L)).astype(np.float64)
+    Wm = rng.integers(-2, 3, (H, L)) / 16.0
+    C = rng.integers(-512, 513, (T, H)) / 8.0
+    d = dict(partials=synth.to_bf16_bits(A), norm_w=None, W=synth.to_bf16_bits(Wm),
+             out=synth.to_bf16_bits(C))
+    wl = synth.Workload("dyadic", T=T, L=L, H=H, P=2, c0=64, n=520, ld_out=H, norm=False)
+    di = DevInputs(d)
+    say("dyadic T=%d" % T)
+    binding.check(di.call(wl))
+    _sync()
+    ref = oracle.latent_tail(d["partials"], None, 0.0, d["W"], wl.c0, wl.n, d["out"])
+    np.testing.assert_array_equal(host(di.out), ref)
+
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_constant_rows_normalise_to_weight(T):
+    """Constant rows normalise to +-w (c^2 >> eps) and zero rows to 0; seen
+    bit-exactly through W = I."""
+    L = 512
+    rng = np.random.Generator(np.random.PCG64(5))
+    nw = synth.to_bf16_bits(1 + 0.2 * rng.standard_normal(L))
+    cs = np.resize(np.array([1.5, -0.75, 0.0, 40.0, -3.0]), T)
+    parts = synth.to_bf16_bits(np.repeat(cs[:, None], L, axis=1))[None]
+    d = dict(partials=parts, norm_w=nw, W=synth.to_bf16_bits(np.eye(L)),
+             out=np.zeros((T, L), np.uint16))
+    di = DevInputs(d)
+    wl = synth.Workload("const", T=T, L=L, H=L, P=1, c0=0, n=L, ld_out=L)
+    say("constant rows T=%d" % T)
+    binding.check(di.call(wl))
+    _sync()
+    got = host(di.out)
+    for t, c in enumerate(cs):
+        if c > 0:
+            np.testing.assert_array_equal(got[t], nw)
+        elif c < 0:
+            np.testing.assert_array_equal(got[t], nw ^ 0x8000)
+        else:
+            assert np.all(synth.bf16_bits_to_f64(got[t]) == 0.0)
+
+
+@pytest.mark.parametrize("T", [8, 257])
+def test_shards_concatenate_bit_exact(T):
+    """Eight column shards c0 = k*H/8 written in turn equal the full call bit
+    for bit (the accumulation order of an element does not depend on the
+    window)."""
+    wl = synth.Workload("shards", T=T, L=1024, H=1792, P=2, c0=0, n=1792, ld_out=1800,
+                        part_std=0.7)
+    d = synth.generate(wl, seed=6)
+    full = DevInputs(d)
+    say("shards T=%d full" % T)
+    binding.check(full.call(wl))
+    part = DevInputs(d)
+    for k in range(8):
+        binding.check(part.call(wl, c0=k * 224, n=224))
+    _sync()
+    np.testing.assert_array_equal(host(part.out), host(full.out))
+
+
+@pytest.mark.parametrize("T", [7, 130])
+def test_split_partials_bit_exact(T):
+    """[X, Y, -Y] and [X/2, X/2] give the same bits as [X]."""
+    wl = synth.Workload("split", T=T, L=1024, H=512, P=1, c0=0, n=512, ld_out=512)
+    d = synth.generate(wl, seed=7)
+    X = d["partials"]
+    Y = synth.generate(wl, seed=8)["partials"]
+    half = synth.to_bf16_bits(synth.bf16_bits_to_f64(X) / 2)
+    results = []
+    for parts in (X, np.concatenate([X, Y, Y ^ 0x8000]), np.concatenate([half, half])):
+        dd = dict(d, partials=parts)
+        di = DevInputs(dd)
+        say("split partials T=%d P=%d" % (T, parts.shape[0]))
+        binding.check(di.call(wl))
+        _sync()
+        results.append(host(di.out))
+    np.testing.assert_array_equal(results[1], results[0])
+    np.testing.assert_array_equal(results[2], results[0])
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,L,H,P,c0,n,ld", [
+    (3, 8, 40, 1, 1, 5, 45),          # smallest latent, odd window
+    (9, 72, 100, 2, 37, 63, 101),     # ragged latent (not a multiple of 64/128)
+    (70, 72, 100, 3, 0, 100, 100),    # same, GEMM path
+    (5, 2048, 300, 1, 13, 257, 333),  # widest latent, skinny
+    (90, 2048, 300, 2, 13, 257, 333), # widest latent, GEMM
+    (1, 1024, 7168, 1, 7167, 1, 7168),  # last column only
+    (33, 1024, 520, 1, 3, 517, 523),  # odd c0 and stride: scalar epilogue
+    (129, 1024, 520, 1, 3, 517, 523), # same on the GEMM path
+    (300, 1024, 1000, 5, 8, 991, 1016),
+])
+def test_edge_shapes(T, L, H, P, c0, n, ld):
+    wl = synth.Workload("edge", T=T, L=L, H=H, P=P, c0=c0, n=n, ld_out=ld, part_std=0.6)
+    _, got, ref = _run_full(wl, seed=T + L)
+    assert_window_close(got, ref, c0, n, "edge T=%d L=%d" % (T, L))
+
+
+def test_sentinels_outside_window_survive():
+    """NaN payloads, -0.0 and +-9984 outside the window and in the padding."""
+    from oracle import oracle
+
+    T, L, H, ld = 70, 256, 96, 103
+    wl = synth.Workload("sent", T=T, L=L, H=H, P=1, c0=17, n=41, ld_out=ld)
+    d = synth.generate(wl, seed=9)
+    sentinels = np.array([0x7FA1, 0xFFC3, 0x8000, 0x461C, 0xC61C, 0x0001], dtype=np.uint16)
+    out = np.resize(sentinels, (T, ld)).astype(np.uint16)
+    out[:, 17:58] = d["out"][:, 17:58]
+    d["out"] = out
+    for thr in (1000, 0):
+        binding.lt_set_skinny_max_tokens(thr)
+        di = DevInputs(d)
+        say("sentinels thr=%d" % thr)
+        binding.check(di.call(wl))
+        _sync()
+        ref = oracle.latent_tail(d["partials"], d["norm_w"], eps32(wl), d["W"], 17, 41, out)
+        assert_window_close(host(di.out), ref, 17, 41, "sentinels thr=%d" % thr)
+    binding.lt_set_skinny_max_tokens(-1)
+
+
+def test_empty_calls_launch_nothing():
+    wl = synth.WORKLOADS["tiny"]
+    d = synth.generate(wl, seed=10)
+    di = DevInputs(d)
+    say("empty calls")
+    assert di.call(wl, T=0) == binding.LT_OK
+    assert di.call(wl, n=0) == binding.LT_OK
+    _sync()
+    np.testing.assert_array_equal(host(di.out), d["out"])
+
+
+def test_invalid_arguments_leave_out_untouched():
+    wl = synth.WORKLOADS["tiny"]
+    d = synth.generate(wl, seed=11)
+    di = DevInputs(d)
+    P, T, L = d["partials"].shape
+    say("invalid arguments")
+    cases = [
+        dict(c0=100, n=29),                     # window beyond H
+        dict(eps=float("nan")),
+        dict(eps=-1.0),
+    ]
+    for kw in cases:
+        assert di.call(wl, **kw) == binding.LT_ERR_INVALID_ARG, kw
+    # misaligned W
+    assert binding.lt_latent_tail(di.partials, P, T, L, di.norm_w, 1e-6, di.W.data_ptr() + 2,
+                                  wl.H - 1, 0, 4, di.out, wl.ld_out) == binding.LT_ERR_UNSUPPORTED
+    # out overlapping W
+    assert binding.lt_latent_tail(di.partials, P, T, L, di.norm_w, 1e-6, di.W, wl.H, 0, 4,
+                                  di.W, wl.ld_out) == binding.LT_ERR_INVALID_ARG
+    # L not a multiple of 8
+    assert binding.lt_latent_tail(di.partials, P, T, L - 4, di.norm_w, 1e-6, di.W, wl.H, 0, 4,
+                                  di.out, wl.ld_out) == binding.LT_ERR_UNSUPPORTED
+    _sync()
+    np.testing.assert_array_equal(host(di.out), d["out"])
+
+
+# --------------------------------------------------------------------------
+# determinism, streams, graph capture
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [16, 1000])
+def test_bitwise_deterministic(T):
+    wl = synth.WORKLOADS["decode"].with_T(T)
+    d = synth.generate(wl, seed=12)
+    di = DevInputs(d)
+    outs = []
+    for _ in range(3):
+        di.reset_out()
+        say("determinism T=%d" % T)
+        binding.check(di.call(wl))
+        _sync()
+        outs.append(host(di.out))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_non_default_stream():
+    import torch
+
+    wl = synth.WORKLOADS["shard"]
+    d = synth.generate(wl, seed=13)
+    di = DevInputs(d)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    say("side stream")
+    binding.check(di.call(wl, stream=s))
+    s.synchronize()
+    got_side = host(di.out)
+    di.reset_out()
+    binding.check(di.call(wl))
+    _sync()
+    np.testing.assert_array_equal(got_side, host(di.out))
+
+
+@pytest.mark.parametrize("T", [8, 777])
+def test_graph_capture_and_replay(T):
+    """Capture one call into a HIP graph (after lt_reserve) and replay it
+    several times, with eager work and synchronisation between replays; every
+    replay must match the eager result."""
+    import torch
+
+    wl = synth.Workload("graph", T=T, L=1024, H=2048, P=2, c0=512, n=1024, ld_out=2048,
+                        part_std=0.7)
+    d = synth.generate(wl, seed=14)
+    di = DevInputs(d)
+    say("graph eager T=%d" % T)
+    binding.check(di.call(wl))
+    _sync()
+    expected = host(di.out)
+
+    s = torch.cuda.Stream()
+    assert binding.lt_reserve(T, wl.L, s) == binding.LT_OK
+    g = torch.cuda.CUDAGraph()
+    di.reset_out()
+    torch.cuda.synchronize()
+    say("graph capture T=%d" % T)
+    with torch.cuda.graph(g, stream=s):
+        status = di.call(wl, stream=torch.cuda.current_stream())
+    assert status == binding.LT_OK
+    for rep in range(4):
+        di.reset_out()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        say("graph replay %d T=%d" % (rep, T))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(di.out), expected)
+        del junk
+    del g
