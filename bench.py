@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the latent-MoE output tail on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+One step = one lt_latent_tail call at every token count of the sweep
+T = 1, 2, 4, ..., 8192 (L=1024, H=7168, full column window n=7168, one
+partial, RMSNorm on, eps=1e-6): every step of the tail runs in every call
+(partial sum, bf16 round trip, RMSNorm, projection, beta-add), the small
+token counts on the weight-streaming kernel and the large ones on the
+sum+RMSNorm kernel followed by the MFMA GEMM.
+
+Inputs are seeded synthetic bf16 data (latent_moe_output_amd.synth, decode
+recipe at T=8192, the smaller T take its first rows), resident in HBM before
+the timed region.  To measure HBM rather than the 256 MB Infinity Cache,
+every call reads a different copy of W (a pool of 48 copies, 704 MB) and
+rotates through enough copies of its partials/out to cycle >= 512 MB.
+
+Printed: ONE JSON line on stdout.  `value` is the whole-job throughput:
+algorithmic flops of the K timed steps / wall-clock time between two device
+synchronisations.  Per-T figures come from HIP events recorded on the
+benchmark stream around each call and, through lt_set_kernel_events, around
+its projection kernel.  `roofline` is for the dominant kernel (k_gemm at
+T=8192); `roofline_skinny` for the weight-streaming kernel at T <= 16;
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the T=8192
+call on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "latent-tail TFLOP/s + W-stream GB/s vs roofline, T=1..8192, L=1024, H=7168"
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, MI355X dense bf16
+T_SWEEP = [1 << i for i in range(14)]
+L, H, P, EPS = 1024, 7168, 1, 1e-6
+N_WPOOL = 48
+ROTATE_BYTES = 512 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops_of(T, n=H, L_=L):
+    return 2 * T * L_ * n
+
+
+def bytes_of(T, n=H, L_=L, P_=P, norm=True):
+    """Algorithmic HBM bytes of one call: W window once, every partial once,
+    the norm weight, a read and a write of the out window."""
+    return 2 * n * L_ + 2 * P_ * T * L_ + 4 * T * n + (2 * L_ if norm else 0)
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs (events), via ctypes."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError("hipEventCreate failed: %d" % rc)
+        return ev.value
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def cpu_baseline(d, target_s=12.0):
+    """The fp64 oracle as it stands on this host's cores, on the first S tokens
+    of the T=8192 call (S sized for ~target_s seconds of work)."""
+    from oracle import oracle
+
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    cal_T = 16
+    t0 = time.perf_counter()
+    oracle.latent_tail(d["partials"][:, :cal_T], d["norm_w"], EPS, d["W"], 0, H,
+                       d["out"][:cal_T])
+    cal = time.perf_counter() - t0
+    S = int(max(cal_T, min(8192, cal_T * target_s / max(cal, 1e-6))))
+    S = max(cal_T, (S // 16) * 16)
+    t0 = time.perf_counter()
+    oracle.latent_tail(d["partials"][:, :S], d["norm_w"], EPS, d["W"], 0, H, d["out"][:S])
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops_of(S) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "first %d of the 8192 tokens of the T=8192 call (L=1024, n=7168, one "
+                  "partial, RMSNorm on), fp64 C oracle, %d OpenMP threads, %.2f s" % (S, threads, dt),
+        "seconds": dt,
+        "tokens": S,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the tail on one GPU only: the kernel works on one GPU's "
+              "share at its real shape and nothing here talks to a second GPU "
+              "(requested --gpus %d)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from latent_moe_output_amd import binding, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    binding.lt_set_skinny_max_tokens(-1)
+    hip = Hip()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev)
+    sh = stream.cuda_stream
+
+    wl = synth.WORKLOADS["decode"].with_T(max(T_SWEEP))
+    log("generating inputs ...")
+    d = synth.generate(wl, seed=0)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).to(dev)
+
+    with torch.cuda.stream(stream):
+        W0 = to_dev(d["W"])
+        wpool = [W0] + [W0.clone() for _ in range(N_WPOOL - 1)]
+        norm_w = to_dev(d["norm_w"])
+        part_all = to_dev(d["partials"])
+        out_all = to_dev(d["out"])
+        sets = {}
+        for T in T_SWEEP:
+            per = 2 * P * T * L + 2 * T * H
+            R = int(min(48, max(2, math.ceil(ROTATE_BYTES / per))))
+            sets[T] = [(part_all[:, :T].clone(), out_all[:T].clone()) for _ in range(R)]
+    del part_all, out_all
+    st = binding.lt_reserve(max(T_SWEEP), L, sh)
+    binding.check(st)
+    torch.cuda.synchronize()
+    log("inputs resident: W pool %d x %.1f MB, rotation sets %s" % (
+        N_WPOOL, 2 * H * L / 1e6, {T: len(v) for T, v in sets.items()}))
+
+    counter = [0]
+
+    def call(T, step):
+        p, o = sets[T][step % len(sets[T])]
+        W = wpool[counter[0] % N_WPOOL]
+        counter[0] += 1
+        return binding.lt_latent_tail(p, P, T, L, norm_w, EPS, W, H, 0, H, o, H, sh)
+
+    # ---- warmup
+    for s in range(args.warmup):
+        for T in T_SWEEP:
+            binding.check(call(T, s))
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    K = args.steps
+    nT = len(T_SWEEP)
+    ev = [[[hip.event() for _ in range(4)] for _ in range(nT)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        for i, T in enumerate(T_SWEEP):
+            e = ev[s][i]
+            hip.record(e[0], sh)
+            binding.lt_set_kernel_events(e[1], e[2])
+            st = call(T, s)
+            binding.lt_set_kernel_events(None, None)
+            hip.record(e[3], sh)
+            if st != binding.LT_OK:
+                raise binding.LtError(st)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+
+    per_T = []
+    call_us = {}
+    kern_us = {}
+    for i, T in enumerate(T_SWEEP):
+        c = [hip.elapsed_ms(ev[s][i][0], ev[s][i][3]) * 1e3 for s in range(K)]
+        k = [hip.elapsed_ms(ev[s][i][1], ev[s][i][2]) * 1e3 for s in range(K)]
+        call_us[T] = float(np.mean(c))
+        kern_us[T] = float(np.mean(k))
+        f, b = flops_of(T), bytes_of(T)
+        roof_us = max(b / HBM_PEAK, f / MFMA_BF16_PEAK) * 1e6
+        per_T.append({
+            "T": T,
+            "path": "skinny" if binding.lt_path_for(T, H) == 1 else "norm+gemm",
+            "call_us": round(call_us[T], 3),
+            "kernel_us": round(kern_us[T], 3),
+            "call_us_median": round(float(np.median(c)), 3),
+            "tflops": round(f / call_us[T] / 1e6, 2),
+            "w_stream_gbps": round(2 * H * L / call_us[T] / 1e3, 1),
+            "alg_gbps": round(b / call_us[T] / 1e3, 1),
+            "roofline_us": round(roof_us, 3),
+            "bound": "hbm" if b / HBM_PEAK > f / MFMA_BF16_PEAK else "mfma",
+            "frac_of_roofline": round(roof_us / call_us[T], 3),
+        })
+    for row in ev:
+        for e4 in row:
+            for e in e4:
+                hip.destroy(e)
+
+    total_flops = K * sum(flops_of(T) for T in T_SWEEP)
+    total_w = K * nT * 2 * H * L
+    value = total_flops / wall / 1e12
+
+    Tg = max(T_SWEEP)
+    g_ach = flops_of(Tg) / (kern_us[Tg] * 1e-6)
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(g_ach / 1e12, 2),
+        "peak": MFMA_BF16_PEAK / 1e12,
+        "unit": "TFLOP/s",
+        "frac": round(g_ach / MFMA_BF16_PEAK, 4),
+        "traffic": None,
+        "kernel": "k_gemm<256,256> (T=8192, L=1024, n=7168)",
+        "avg_launch_us": round(kern_us[Tg], 3),
+        "flops_per_launch": flops_of(Tg),
+    }
+    sk = [T for T in T_SWEEP if T <= 16]
+    sk_bytes = sum(bytes_of(T) for T in sk)
+    sk_us = sum(kern_us[T] for T in sk)
+    roofline_skinny = {
+        "bound": "hbm",
+        "achieved": round(sk_bytes / (sk_us * 1e-6) / 1e9, 1),
+        "peak": HBM_PEAK / 1e9,
+        "unit": "GB/s",
+        "frac": round(sk_bytes / (sk_us * 1e-6) / HBM_PEAK, 4),
+        "traffic": None,
+        "kernel": "k_skinny<8,1> (T=1,2,4,8,16; L=1024, n=7168)",
+        "avg_launch_us": round(sk_us / len(sk), 3),
+        "bytes_per_launch_avg": sk_bytes // len(sk),
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16, decode recipe; W pool of 48 copies + rotated "
+                "partials/out so every call reads HBM, not the Infinity Cache)",
+        "config": {
+            "workload": "latent-MoE tail, T sweep 1..8192 (powers of 2), L=1024, H=7168, "
+                        "full window c0=0 n=7168, 1 partial, RMSNorm on, eps=1e-6",
+            "T_sweep": T_SWEEP, "L": L, "H": H, "n": H, "c0": 0, "n_partials": P,
+            "skinny_max": binding.lt_get_skinny_max_tokens(),
+        },
+        "w_stream_gbps": round(total_w / wall / 1e9, 1),
+        "per_T": per_T,
+        "roofline": roofline,
+        "roofline_skinny": roofline_skinny,
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -139,6 +139,17 @@ LT_API int64_t lt_get_skinny_max_tokens(void);
  */
 LT_API int lt_path_for(int64_t T, int64_t n);
 
+/*
+ * lt_set_kernel_events -- timing hook for benchmarks and profilers.  While set
+ * (non-NULL), every lt_latent_tail call records the hipEvent_t `before` on its
+ * stream immediately before launching its projection kernel (k_skinny, or
+ * k_gemm on the large-token path) and `after` immediately after it, so the
+ * caller can time that kernel alone with hipEventElapsedTime.  Pass NULL, NULL
+ * to switch it off (the default).  Process-wide; not for concurrent callers.
+ * Returns LT_OK.
+ */
+LT_API int lt_set_kernel_events(void *before, void *after);
+
 /* Library version string, e.g. "liblatenttail 0.1.0 gfx950". */
 LT_API const char *lt_version(void);
 

@@ -58,6 +58,8 @@ def load():
     lib.lt_get_skinny_max_tokens.restype = i64
     lib.lt_path_for.argtypes = [i64, i64]
     lib.lt_path_for.restype = ctypes.c_int
+    lib.lt_set_kernel_events.argtypes = [vp, vp]
+    lib.lt_set_kernel_events.restype = ctypes.c_int
     lib.lt_version.argtypes = []
     lib.lt_version.restype = ctypes.c_char_p
     _lib = lib
@@ -116,6 +118,11 @@ def lt_get_skinny_max_tokens() -> int:
 
 def lt_path_for(T, n) -> int:
     return int(load().lt_path_for(int(T), int(n)))
+
+
+def lt_set_kernel_events(before, after) -> int:
+    """before/after: raw hipEvent_t handles (ints) or None."""
+    return int(load().lt_set_kernel_events(before, after))
 
 
 def lt_version() -> str:

@@ -28,6 +28,15 @@ namespace {
 constexpr int64_t kDefaultSkinnyMax = 64;
 
 std::atomic<int64_t> g_skinny_max{-1};
+std::atomic<void *> g_ev_before{nullptr};
+std::atomic<void *> g_ev_after{nullptr};
+
+// Records the benchmark timing event `which` (if set) on `s`.
+bool record_hook(const std::atomic<void *> &which, hipStream_t s)
+{
+    void *ev = which.load(std::memory_order_relaxed);
+    return !ev || hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) == hipSuccess;
+}
 
 int64_t default_skinny_max()
 {
@@ -133,6 +142,13 @@ int64_t lt_set_skinny_max_tokens(int64_t t)
 
 int64_t lt_get_skinny_max_tokens(void) { return skinny_max(); }
 
+int lt_set_kernel_events(void *before, void *after)
+{
+    g_ev_before.store(before, std::memory_order_relaxed);
+    g_ev_after.store(after, std::memory_order_relaxed);
+    return LT_OK;
+}
+
 int lt_path_for(int64_t T, int64_t n)
 {
     if (T <= 0 || n <= 0) return 0;
@@ -207,13 +223,14 @@ int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
     (void)hipGetLastError();  // start from a clean error state
     if (T <= skinny_max()) {
         const int per = lt::skinny_tokens_per_launch((int)L);
+        if (!record_hook(g_ev_before, s)) return LT_ERR_HIP;
         for (int64_t tb = 0; tb < T; tb += per) {
             const int tc = (int)((T - tb) < per ? (T - tb) : per);
             hipError_t e = lt::launch_skinny(part + tb * L, tl, n_partials, tc, (int)L, nw, eps,
                                              Wn, (int)n, outn + tb * ld_out, ld_out, s);
             if (e != hipSuccess) return LT_ERR_HIP;
         }
-        return LT_OK;
+        return record_hook(g_ev_after, s) ? LT_OK : LT_ERR_HIP;
     }
 
     void *scratch = nullptr;
@@ -222,9 +239,10 @@ int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
     uint16_t *y = static_cast<uint16_t *>(scratch);
     if (lt::launch_sum_rmsnorm(part, tl, n_partials, T, (int)L, nw, eps, y, s) != hipSuccess)
         return LT_ERR_HIP;
+    if (!record_hook(g_ev_before, s)) return LT_ERR_HIP;
     if (lt::launch_gemm(y, T, (int)L, Wn, (int)n, outn, ld_out, s) != hipSuccess)
         return LT_ERR_HIP;
-    return LT_OK;
+    return record_hook(g_ev_after, s) ? LT_OK : LT_ERR_HIP;
 }
 
 }  // extern "C"
