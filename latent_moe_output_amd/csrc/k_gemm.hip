@@ -8,32 +8,53 @@
 //
 // Layout on gfx950:
 //  * Workgroup tile BJ (W rows = output columns) x BT (tokens), 4 waves in a
-//    2 x 2 grid, K step 64.  Each wave owns (BJ/2) x (BT/2) as 32 x 32 tiles of
-//    v_mfma_f32_32x32x16_bf16 with W as the A operand and the latent as B, so
-//    a lane's accumulators run along the output row.
-//  * Global -> registers -> LDS, two LDS stages, one barrier per K step; the
-//    next step's loads are in flight while the current step multiplies.  A
-//    row of a stage is 64 bf16 = eight 16-byte chunks, stored XOR-swizzled so
-//    the fragment reads of 8 consecutive lanes hit 8 different chunk slots.
+//    2 x 2 grid.  Each wave owns (BJ/2) x (BT/2) as 32 x 32 tiles of
+//    v_mfma_f32_32x32x16_bf16 with W as the A operand and the latent as B.
+//  * K advances 32 at a time through NS = 4 LDS stages filled straight from
+//    HBM/L2 by buffer_load_dwordx4 ... lds, so three stages are in flight
+//    while one is multiplied.  Buffer resources are clipped per workgroup:
+//    rows past the end of W's window or past T read as zero with no branch.
+//  * A stage row is 32 bf16 = four 16-byte chunks; each direct load writes
+//    1 KB (16 rows) contiguously, and the chunk a lane fetches is chosen so
+//    the rows land XOR-swizzled.  Fragments of both operands are read from
+//    rows perm32(lane % 32) of each 32-row block, which with the XOR key is
+//    free of bank conflicts (so the latent's token order inside a block is
+//    permuted the same way; the epilogue follows it).
+//  * One barrier per K step, placed between the step's two MFMA halves: the
+//    second half's fragments are read before it and the next step's first
+//    fragments right after it, so LDS latency hides behind MFMA work.
 //  * A-operand rows are read through a fixed permutation of the 32 rows of a
-//    tile chosen so that each lane ends up holding 16 consecutive output
-//    columns (two runs of 8): the epilogue is then 16-byte loads and stores of
-//    `out`, and lanes l and l+32 cover 32 contiguous bytes of a row.
-//  * Ragged edges (tokens >= T, columns >= n, k >= L) are zero-filled on load
-//    and masked on store; nothing outside [c0, c0+n) x [0, T) is written.
+//    tile so that each lane holds 16 consecutive output columns (two runs of
+//    8).  The `out` tile is read in that layout with 16-byte loads during the
+//    last three K steps; the sums are rounded, staged in LDS (swizzled) and
+//    written back row by row, so every store instruction covers whole
+//    contiguous row segments of `out`.
+//  * Ragged edges are masked on store; nothing outside [c0, c0+n) x [0, T) is
+//    written.
 //  * Tiles are spread so that each of the 8 XCDs receives a contiguous range
 //    of the (grouped) tile order, keeping W and latent blocks that are reused
 //    by neighbouring tiles in the same XCD's L2.
 // Each output element's accumulation order depends on (L, tile config) only,
 // not on c0 or n.
+#include <type_traits>
+
 #include "lt_device.h"
 #include "lt_internal.h"
 
 namespace lt {
 namespace {
 
-constexpr int BK = 64;
+constexpr int BK = 32;                    // K per stage
+constexpr int NS = 4;                     // LDS stages
+constexpr int ROWB = BK * 2;              // bytes per stage row
 constexpr int NUM_XCD = 8;
+constexpr uint32_t RSRC_W3 = LT_RSRC_W3;
+constexpr uint32_t OOB = LT_OOB;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int V> using I = std::integral_constant<int, V>;
+template <bool V> using B = std::integral_constant<bool, V>;
 
 // Row permutation of a 32-row A tile: MFMA row m reads LDS row perm32(m).
 __device__ __forceinline__ int perm32(int m)
@@ -41,20 +62,37 @@ __device__ __forceinline__ int perm32(int m)
     const int q = m >> 3, hh = (m >> 2) & 1, alo = m & 3;
     return 16 * (q >> 1) + 8 * hh + 4 * (q & 1) + alo;
 }
-// Chunk-slot swizzles (8 slots of 16 bytes per 128-byte stage row).
-__device__ __forceinline__ int swz_a(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int swz_b(int row) { return row & 7; }
+// Chunk-slot XOR key (4 slots of 16 bytes per 64-byte stage row).  Fragment
+// reads of the 32 rows perm32(0..31) with this key are free of LDS bank
+// conflicts on gfx950 (measured); both operands are read that way.
+__device__ __forceinline__ int swz(int r) { return (((r >> 3) & 1) << 1) | (((r >> 1) ^ (r >> 2)) & 1); }
 
-template <int BJ, int BT, int GROUP_J>
+template <int BJ, int BT, int GROUP_J, bool KTAIL, bool EPI_LDS>
 __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t T, int L,
                                               const u16 *__restrict__ Wn, int n,
-                                              u16 *__restrict__ outn, int64_t ld_out, int vec16,
-                                              int ntj, int ntt)
+                                              u16 *__restrict__ outn, int64_t ld_out, int ntj,
+                                              int ntt)
 {
     constexpr int MJ = BJ / 64, MT = BT / 64;   // 32x32 tiles per wave
-    constexpr int LA = BJ / 32, LB = BT / 32;   // 16-byte loads per thread per stage
-    __shared__ __attribute__((aligned(16))) u16 sA[2][BJ * BK];
-    __shared__ __attribute__((aligned(16))) u16 sB[2][BT * BK];
+    constexpr int LA = BJ / 64, LB = BT / 64;   // direct loads per thread per stage
+    constexpr int LPS = LA + LB;
+    constexpr int STAGE_A = BJ * ROWB, STAGE = (BJ + BT) * ROWB;
+    constexpr int NFR = MJ + MT, NMF = MJ * MT;
+    // One __shared__ array per stage, always indexed by a compile-time stage
+    // number: the compiler can then tell which array a direct load writes and
+    // waits only for the loads of the stage it is about to read.
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+    __shared__ __attribute__((aligned(1024))) char st3[STAGE];
+    static_assert(NS == 4, "four stage arrays");
+    static_assert(STAGE >= (BT / 4) * BJ * 2, "a quarter of the out tile must fit a stage");
+    auto stage = [&](auto S) __attribute__((always_inline)) -> char * {
+        if constexpr (decltype(S)::value == 0) return st0;
+        else if constexpr (decltype(S)::value == 1) return st1;
+        else if constexpr (decltype(S)::value == 2) return st2;
+        else return st3;
+    };
 
     // ---- tile coordinates: XCD-contiguous ranges, then GROUP_J-wide groups
     const int G = ntj * ntt;
@@ -73,39 +111,79 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
     const int64_t t0 = (int64_t)tt * BT;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63;
+    const int l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wj = w >> 1, wt = w & 1;
     const int nchunk = L >> 3;
-    const int nk = (L + BK - 1) / BK;
+    // K steps, padded to whole trips of NS steps; padded steps read zeros
+    // (KTAIL masking), so every trip has the same straight-line body.
+    const int nk = ((L + BK * NS - 1) / (BK * NS)) * NS;
+    const uint32_t row_bytes = (uint32_t)L * 2u;
 
-    const int lrow = tid >> 3, lch = tid & 7;
-    u32x4_t ra[LA], rb[LB];
+    // ---- buffer resources clipped to this tile's rows: overhanging rows read 0
+    const int rows_a = min(BJ, n - j0);
+    const int rows_b = (int)min((int64_t)BT, T - t0);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Wn + (int64_t)j0 * L), (short)0, (int)((uint32_t)rows_a * row_bytes), RSRC_W3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Y + t0 * L), (short)0, (int)((uint32_t)rows_b * row_bytes), RSRC_W3);
 
-    auto gload = [&](int kb) {
-        const int c = kb * 8 + lch;
-        const bool kok = c < nchunk;
+    // ---- direct loads: lane i of wave w, load q -> stage row 64q + 16w + i/4,
+    // LDS slot i%4, global chunk (slot ^ key(row)).
+    const int lrow = 16 * w + (l >> 2);
+    const int lslot = l & 3;
+    uint32_t offa[LA], offb[LB];
+    int cha[LA], chb[LB];
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+        const int row = 64 * q + lrow;
+        cha[q] = lslot ^ swz(row);
+        offa[q] = (uint32_t)row * row_bytes + (uint32_t)cha[q] * 16u;
+    }
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+        const int row = 64 * q + lrow;
+        chb[q] = lslot ^ swz(row);
+        offb[q] = (uint32_t)row * row_bytes + (uint32_t)chb[q] * 16u;
+    }
+    auto issue = [&](auto S, int s) __attribute__((always_inline)) {   // stage s goes to array S = s % NS
+        char *sa = stage(S);
+        char *sb = sa + STAGE_A;
+        const uint32_t kbyte = (uint32_t)s * ROWB;
 #pragma unroll
         for (int q = 0; q < LA; ++q) {
-            const int j = j0 + lrow + 32 * q;
-            ra[q] = (kok && j < n) ? lt_load16(Wn + (int64_t)j * L + c * 8) : u32x4_t{0, 0, 0, 0};
+            uint32_t vo = offa[q] + kbyte;
+            if (KTAIL && s * 4 + cha[q] >= nchunk) vo = OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (64 * q + 16 * w) * ROWB),
+                                                     16, vo, 0, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < LB; ++q) {
-            const int64_t t = t0 + lrow + 32 * q;
-            rb[q] = (kok && t < T) ? lt_load16(Y + t * L + c * 8) : u32x4_t{0, 0, 0, 0};
+            uint32_t vo = offb[q] + kbyte;
+            if (KTAIL && s * 4 + chb[q] >= nchunk) vo = OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + (64 * q + 16 * w) * ROWB),
+                                                     16, vo, 0, 0, 0);
         }
     };
-    auto lstore = [&](int st) {
+
+    // ---- fragment reads (byte offsets within a stage)
+    const int hsel = l >> 5;
+    const int arow = wj * (BJ / 2) + perm32(l & 31);
+    const int brow = wt * (BT / 2) + perm32(l & 31);   // token of this lane's D column
+    int afr[2], bfr[2];
 #pragma unroll
-        for (int q = 0; q < LA; ++q) {
-            const int row = lrow + 32 * q;
-            *reinterpret_cast<u32x4_t *>(&sA[st][row * BK + ((lch ^ swz_a(row)) << 3)]) = ra[q];
-        }
+    for (int ks = 0; ks < 2; ++ks) {
+        afr[ks] = arow * ROWB + (((2 * ks + hsel) ^ swz(arow)) << 4);
+        bfr[ks] = STAGE_A + brow * ROWB + (((2 * ks + hsel) ^ swz(brow)) << 4);
+    }
+    auto read_frags = [&](auto S, int ks, bf16x8_t (&fa)[MJ], bf16x8_t (&fb)[MT]) {
+        const char *base = stage(S);
 #pragma unroll
-        for (int q = 0; q < LB; ++q) {
-            const int row = lrow + 32 * q;
-            *reinterpret_cast<u32x4_t *>(&sB[st][row * BK + ((lch ^ swz_b(row)) << 3)]) = rb[q];
-        }
+        for (int mj = 0; mj < MJ; ++mj)
+            fa[mj] = *reinterpret_cast<const bf16x8_t *>(base + afr[ks] + mj * 32 * ROWB);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            fb[mt] = *reinterpret_cast<const bf16x8_t *>(base + bfr[ks] + mt * 32 * ROWB);
     };
 
     f32x16_t acc[MJ][MT];
@@ -113,66 +191,195 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
     for (int mj = 0; mj < MJ; ++mj)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mj][mt] = f32x16_t{};
+    auto mfma_all = [&](const bf16x8_t (&fa)[MJ], const bf16x8_t (&fb)[MT]) {
+#pragma unroll
+        for (int mj = 0; mj < MJ; ++mj)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mj][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mj], fb[mt], acc[mj][mt],
+                                                                      0, 0, 0);
+    };
 
-    const int arow0 = wj * (BJ / 2) + perm32(l & 31);
-    const int brow0 = wt * (BT / 2) + (l & 31);
-    const int hsel = l >> 5;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int kb = 0; kb < nk; ++kb) {
-        const int st = kb & 1;
-        if (kb + 1 < nk) gload(kb + 1);
+    // ---- the out tile goes through LDS.  Quarter q (tile rows q*BT/4 ..,
+    // row-major, 16-byte chunks XOR-swizzled by row) arrives by direct loads in
+    // the stage array that tail step q has just freed, so its HBM latency
+    // overlaps the last MFMAs; the sums are then formed in place and the tile
+    // is written back row by row.
+    constexpr int CPRE = BJ / 8;               // 16-byte chunks per tile row
+    constexpr int RPQ = BT / 4;                // tile rows per quarter
+    constexpr int QCH = RPQ * CPRE;            // chunks per quarter
+    constexpr int QLD = QCH / 256;             // direct loads per thread per quarter
+    static_assert(!EPI_LDS || QCH % 256 == 0, "a quarter is whole workgroup loads");
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(outn + t0 * ld_out), (short)0,
+        (int)(((int64_t)max(rows_b - 1, 0) * ld_out + n) * 2), RSRC_W3);
+    auto load_c_quarter = [&](char *dst, int q) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = 2 * ks + hsel;
-            bf16x8_t fa[MJ], fb[MT];
-#pragma unroll
-            for (int mj = 0; mj < MJ; ++mj) {
-                const int row = arow0 + 32 * mj;
-                fa[mj] = *reinterpret_cast<const bf16x8_t *>(
-                    &sA[st][row * BK + ((ch ^ swz_a(row)) << 3)]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int row = brow0 + 32 * mt;
-                fb[mt] = *reinterpret_cast<const bf16x8_t *>(
-                    &sB[st][row * BK + ((ch ^ swz_b(row)) << 3)]);
-            }
-#pragma unroll
-            for (int mj = 0; mj < MJ; ++mj)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[mj][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mj], fb[mt],
-                                                                          acc[mj][mt], 0, 0, 0);
+        for (int it = 0; it < QLD; ++it) {
+            const int idx0 = it * 256 + 64 * w;     // wave-uniform
+            const int idx = idx0 + l;
+            const int r = q * RPQ + idx / CPRE;
+            const int c = (idx % CPRE) ^ (r & (CPRE - 1));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rc, (lds_void *)(dst + idx0 * 16), 16,
+                (uint32_t)(((int64_t)r * ld_out + j0 + 8 * c) * 2), 0, 0, 0);
         }
-        if (kb + 1 < nk) lstore(st ^ 1);
-        __syncthreads();
+    };
+    auto stage_dyn = [&](int i) __attribute__((always_inline)) -> char * {
+        return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3;
+    };
+
+    // One K step on stage array S (= kb % NS): MFMA half 0 (fragments already
+    // in f0), barrier for the next stage between the halves, MFMA half 1.  The
+    // array freed by the previous step (SP) receives stage kb+NS-1 (CQ < 0),
+    // quarter CQ of the out tile (0 <= CQ < 4), or nothing.  WAIT is the
+    // number of vector loads allowed to stay in flight at the barrier; the
+    // last step (LAST) has no barrier.
+    bf16x8_t f0a[MJ], f0b[MT], f1a[MJ], f1b[MT];
+    auto step = [&](auto S, auto CQ, auto WAIT, auto LAST, int kb) __attribute__((always_inline)) {
+        constexpr int s = decltype(S)::value;
+        constexpr int cq = decltype(CQ)::value;
+        using SN = std::integral_constant<int, (s + 1) % NS>;
+        using SP = std::integral_constant<int, (s + NS - 1) % NS>;
+        if constexpr (cq < 0) issue(SP{}, kb + NS - 1);
+        else if constexpr (cq < 4) load_c_quarter(stage(SP{}), cq);
+        read_frags(S, 1, f1a, f1b);
+        mfma_all(f0a, f0b);
+#pragma unroll
+        for (int i = 0; i < NFR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NFR, 0);
+        if constexpr (!decltype(LAST)::value) {
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(decltype(WAIT)::value));
+            lt_lds_barrier();
+            read_frags(SN{}, 0, f0a, f0b);
+        }
+        mfma_all(f1a, f1b);
+        // interleave: half-1 fragment reads between half-0 MFMAs (above), the
+        // next stage's first reads between half-1 MFMAs (below)
+#pragma unroll
+        for (int i = 0; i < NFR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NFR, 0);
+    };
+    // ---- prologue: stages 0 .. NS-2 in flight, wait for stage 0
+    issue(I<0>{}, 0);
+    issue(I<1>{}, 1);
+    issue(I<2>{}, 2);
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0((NS - 2) * LPS));
+    lt_lds_barrier();
+    read_frags(I<0>{}, 0, f0a, f0b);
+
+    // ---- K loop: NS steps per trip (one per stage array), each issuing stage
+    // kb+NS-1 and leaving NS-2 stages in flight.  The last trip is peeled: its
+    // first step issues the last stage, the other three issue no stage but
+    // load out-tile quarters 0..2 into the arrays just freed (arrays 0..2).
+    constexpr int W_MAIN = (NS - 2) * LPS;
+    for (int kb = 0; kb < nk - NS; kb += NS) {
+        step(I<0>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb);
+        step(I<1>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb + 1);
+        step(I<2>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb + 2);
+        step(I<3>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb + 3);
+    }
+    {
+        const int kb = nk - NS;
+        constexpr int C0 = EPI_LDS ? 0 : 4, C1 = EPI_LDS ? 1 : 4, C2 = EPI_LDS ? 2 : 4;
+        constexpr int Q = EPI_LDS ? QLD : 0;
+        step(I<0>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb);
+        step(I<1>{}, I<C0>{}, I<LPS + Q>{}, B<false>{}, kb + 1);
+        step(I<2>{}, I<C1>{}, I<2 * Q>{}, B<false>{}, kb + 2);
+        step(I<3>{}, I<C2>{}, I<0>{}, B<true>{}, kb + 3);
     }
 
-    // ---- epilogue: lane holds columns 16*half + 8*hsel + 0..7 of each tile
+    if constexpr (EPI_LDS) {
+        // quarter 3 goes into array 3 once every wave is done with it
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));   // LDS reads done
+        lt_lds_barrier();
+        load_c_quarter(st3, 3);
+        __builtin_amdgcn_s_waitcnt(0);
+        lt_lds_barrier();
+        auto stage_row = [&](int r) __attribute__((always_inline)) -> char * {
+            return stage_dyn(r / RPQ) + (r % RPQ) * (BJ * 2);
+        };
+        // ---- sums in place: out + acc, one rounding
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int64_t t = t0 + brow0 + 32 * mt;
-        if (t >= T) continue;
-        u16 *orow = outn + t * ld_out;
+        for (int mt = 0; mt < MT; ++mt) {
+            const int r = brow + 32 * mt;
 #pragma unroll
-        for (int mj = 0; mj < MJ; ++mj) {
+            for (int mj = 0; mj < MJ; ++mj) {
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int j = j0 + wj * (BJ / 2) + 32 * mj + 16 * half + 8 * hsel;
-                const f32x16_t &a = acc[mj][mt];
-                if (vec16 && j + 8 <= n) {
-                    const u32x4_t ov = lt_load16(orow + j);
+                for (int half = 0; half < 2; ++half) {
+                    const int c = (wj * (BJ / 2) + 32 * mj + 16 * half + 8 * hsel) >> 3;
+                    const f32x16_t &a = acc[mj][mt];
+                    u32x4_t *ptr = reinterpret_cast<u32x4_t *>(stage_row(r) +
+                                                               ((c ^ (r & (CPRE - 1))) << 4));
+                    u32x4_t ov = *ptr;
+                    // The buffer range check is per dword: a chunk that straddles
+                    // the window end can come back with its last valid column
+                    // zeroed.  Re-read that chunk's valid columns directly.
+                    const int jc = j0 + 8 * c;
+                    if (jc < n && jc + 8 > n && t0 + r < T) {
+                        const u16 *src = outn + (t0 + r) * ld_out + jc;
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2) {
+                            const uint32_t lo = (jc + e < n) ? src[e] : 0u;
+                            const uint32_t hi = (jc + e + 1 < n) ? src[e + 1] : 0u;
+                            ov[e >> 1] = lo | (hi << 16);
+                        }
+                    }
                     u32x4_t nv;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         nv[e] = lt_pack2(lt_bf_lo(ov[e]) + a[8 * half + 2 * e],
                                          lt_bf_hi(ov[e]) + a[8 * half + 2 * e + 1]);
-                    *reinterpret_cast<u32x4_t *>(orow + j) = nv;
+                    *ptr = nv;
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        lt_lds_barrier();
+        // ---- write back whole row segments
+        constexpr int LPR = CPRE;                     // lanes per tile row
+        constexpr int RPI = 64 / LPR;                 // rows per store instruction
+        constexpr int ROWS_W = BT / 4;                // rows per wave
+        static_assert(CPRE <= 64, "row wider than a wave");
+#pragma unroll 4
+        for (int i = 0; i < ROWS_W / RPI; ++i) {
+            const int r = w * ROWS_W + i * RPI + l / LPR;
+            const int c = l % LPR;
+            const int64_t t = t0 + r;
+            const int j = j0 + 8 * c;
+            if (t < T && j < n) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+                    stage_row(r) + ((c ^ (r & (CPRE - 1))) << 4));
+                if (j + 8 <= n) {
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        v, rc, (uint32_t)(((int64_t)r * ld_out + j) * 2), 0, 0);
                 } else {
+                    u16 *o = outn + t * ld_out + j;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (j + e < n) o[e] = (u16)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                }
+            }
+        }
+    } else {
+        // ---- plain epilogue (unaligned `out`): element-wise read-add-round-write
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int64_t t = t0 + brow + 32 * mt;
+            if (t >= T) continue;
+            u16 *orow = outn + t * ld_out;
+#pragma unroll
+            for (int mj = 0; mj < MJ; ++mj) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int j = j0 + wj * (BJ / 2) + 32 * mj + 16 * half + 8 * hsel;
+                    const f32x16_t &a = acc[mj][mt];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         if (j + e < n) {
@@ -188,14 +395,30 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
 
 template <int BJ, int BT, int GROUP_J>
 hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 *outn,
-                      int64_t ld_out, int vec16, hipStream_t stream)
+                      int64_t ld_out, bool vec16, hipStream_t stream)
 {
     const int ntj = (n + BJ - 1) / BJ;
     const int64_t ntt = (T + BT - 1) / BT;
     if ((int64_t)ntj * ntt > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(ntj * ntt)), block(256);
-    hipLaunchKernelGGL((k_gemm<BJ, BT, GROUP_J>), grid, block, 0, stream, y, T, L, Wn, n, outn,
-                       ld_out, vec16, ntj, (int)ntt);
+    // The LDS epilogue moves whole out-tile quarters with workgroup-wide 16-byte
+    // direct loads and addresses `out` through 32-bit buffer offsets: it needs
+    // an aligned window and a tile extent below 2 GiB; anything else (and tiles
+    // too small for whole-workgroup quarters) takes the plain epilogue.
+    constexpr bool EPI_OK = ((BT / 4) * (BJ / 8)) % 256 == 0;
+    const bool epi = EPI_OK && vec16 && (int64_t)BT * ld_out * 2 < ((int64_t)1 << 31);
+#define LT_GEMM_LAUNCH(KT, EPI)                                                              \
+    hipLaunchKernelGGL((k_gemm<BJ, BT, GROUP_J, KT, EPI>), grid, block, 0, stream, y, T, L, Wn, \
+                       n, outn, ld_out, ntj, (int)ntt)
+    const bool kt = L % (BK * NS) != 0;
+    if constexpr (EPI_OK) {
+        if (epi) {
+            if (kt) LT_GEMM_LAUNCH(true, true); else LT_GEMM_LAUNCH(false, true);
+            return hipGetLastError();
+        }
+    }
+    if (kt) LT_GEMM_LAUNCH(true, false); else LT_GEMM_LAUNCH(false, false);
+#undef LT_GEMM_LAUNCH
     return hipGetLastError();
 }
 
@@ -204,7 +427,7 @@ hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 
 hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
                        uint16_t *outn, int64_t ld_out, hipStream_t stream)
 {
-    const int vec16 = ((reinterpret_cast<uintptr_t>(outn) & 15) == 0) && (ld_out % 8 == 0);
+    const bool vec16 = ((reinterpret_cast<uintptr_t>(outn) & 15) == 0) && (ld_out % 8 == 0);
     const int64_t tiles256 = (int64_t)((n + 255) / 256) * ((T + 255) / 256);
     const int64_t tiles128 = (int64_t)((n + 127) / 128) * ((T + 127) / 128);
     if (tiles256 >= 512)

@@ -6,181 +6,173 @@
 // narrow, addmm_).  At these token counts the work is bound by reading the
 // W window from HBM once, so the kernel is built around that stream:
 //
-//  * A workgroup owns 16 rows of the W window (16 output columns).  Its four
-//    waves split the latent width: chunk c (8 elements) goes to wave
-//    (c / 4) % 4, lane group c % 4, step c / 16.  Each lane's W chunks are
-//    loaded straight into registers in the A-operand layout of
+//  * A workgroup owns RW rows of the W window (output columns), RW <= 16*JT:
+//    the window is cut into about one row block per compute unit, so every CU
+//    streams an equal share and the partial tile and norm weight, which every
+//    workgroup needs, are fetched as few times as possible.  Its KW waves
+//    split the latent width: chunk c (8 elements) belongs to wave
+//    (c / 4) % KW, lane group c % 4, step c / (4*KW).  Each lane's W chunks
+//    are loaded straight into registers in the A-operand layout of
 //    v_mfma_f32_16x16x32_bf16 (row = lane % 16, 8 consecutive k per lane), so
-//    W never passes through LDS and each row is read as 64-byte runs.
+//    W never passes through LDS.
 //  * The partial chunks are loaded first, then the norm weight, then all of
-//    the workgroup's W chunks, so the whole W share is in flight while the
-//    latent is being normalised.
+//    the workgroup's W chunks, then the out values the epilogue will add to:
+//    the whole W share is in flight while the latent is normalised, and the
+//    read-modify-write of the window adds no memory round trip at the end.
 //  * The latent is built in registers in the B-operand layout (token = lane
-//    % 16), with the sum of squares reduced lanes -> waves in the fixed slot
-//    tree of lt_device.h.  Tokens ride the MFMA's 16-wide N dimension; the
-//    idle columns of a partly filled token tile cost nothing that matters
-//    here, the MFMA pipe is far from busy.
-//  * The four per-wave partial products are added in LDS in a fixed order
-//    and written with one bf16 rounding onto the window.
+//    % 16) by the shared tile code of lt_latent.h; splitting K over KW waves
+//    keeps each lane's share of the RMSNorm arithmetic small, and the norm's
+//    barrier leaves the W loads in flight.  Tokens ride the MFMA's 16-wide N
+//    dimension; the idle columns of a partly filled token tile cost nothing
+//    that matters here, the matrix cores are far from busy.
+//  * The KW per-wave partial products are added in LDS in wave order and
+//    written with one bf16 rounding onto the window.
 //
 // Every element's accumulation order depends only on (T, L), never on c0 or
 // n, so column shards reproduce the full-window result bit for bit.
-#include "lt_device.h"
 #include "lt_internal.h"
+#include "lt_latent.h"
 
 namespace lt {
 namespace {
 
-template <int NI, int TT>
-__global__ __launch_bounds__(256) void k_skinny(const u16 *__restrict__ part, int64_t pstride,
-                                                int P, int T, int L,
-                                                const u16 *__restrict__ norm_w, float eps,
-                                                float inv_L, const u16 *__restrict__ Wn, int n,
-                                                u16 *__restrict__ outn, int64_t ld_out, int vec8)
+template <int NI, int TT, int JT>
+__global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part, int64_t pstride,
+                                                    int P, int T, int L,
+                                                    const u16 *__restrict__ norm_w, float eps,
+                                                    float inv_L, const u16 *__restrict__ Wn, int n,
+                                                    int RW, u16 *__restrict__ outn, int64_t ld_out,
+                                                    int vec8)
 {
-    const int w = threadIdx.x >> 6;
+    static_assert(JT * TT <= KW, "one epilogue fragment per wave");
     const int l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = l & 15;
     const int g = l >> 4;
     const int nchunk = L >> 3;
-    const int j0 = blockIdx.x * 16;
+    const int j0 = blockIdx.x * RW;
+    const int rows = min(RW, n - j0);   // 1..RW rows of this block are in the window
 
-    __shared__ float red_ss[4][TT * 16];
-    __shared__ f32x4_t red_acc[4][TT][64];
+    __shared__ float red_ss[TT][KW * 16];
+    __shared__ f32x4_t red_acc[KW][JT * TT][64];
 
-    // 1. issue loads: partial 0, norm weight, W rows
+    // 1. partials (summed first when there are several, so that the sum's
+    //    waits cover partial loads only), then norm weight, W rows, out values
     u32x4_t sv[TT][NI];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-        const int t = 16 * tt + r;
+    for (int tt = 0; tt < TT; ++tt) latent_load(part + (int64_t)16 * tt * L, T - 16 * tt, L, sv[tt]);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int c = 16 * i + 4 * w + g;
-            sv[tt][i] = (c < nchunk && t < T) ? lt_load16(part + (int64_t)t * L + c * 8)
-                                              : u32x4_t{0, 0, 0, 0};
-        }
-    }
+    for (int tt = 0; tt < TT; ++tt)
+        latent_sum(part + (int64_t)16 * tt * L, pstride, P, T - 16 * tt, L, sv[tt]);
     u32x4_t wv[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int c = 16 * i + 4 * w + g;
-        wv[i] = (norm_w && c < nchunk) ? lt_load16(norm_w + c * 8) : u32x4_t{0, 0, 0, 0};
-    }
-    u32x4_t wa[NI];
+    if (norm_w) latent_load_weight(norm_w, L, wv);
+    u32x4_t wa[JT][NI];
     {
-        const int j = j0 + r;
+        const __amdgpu_buffer_rsrc_t rw = lt_rsrc(Wn + (int64_t)j0 * L, (uint32_t)(rows * L) * 2u);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int c = 16 * i + 4 * w + g;
-            wa[i] = (c < nchunk && j < n) ? lt_load16(Wn + (int64_t)j * L + c * 8)
-                                          : u32x4_t{0, 0, 0, 0};
-        }
-    }
-
-    // 2. remaining partials, bf16 round trip of the sum, slot sums of squares
-    float ss[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-        const int t = 16 * tt + r;
-        ss[tt] = 0.f;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int c = 16 * i + 4 * w + g;
-            if (c < nchunk && t < T) {
-                float s[8];
-                lt_unpack8(sv[tt][i], s);
-                if (P > 1) {
-                    const u16 *p0 = part + (int64_t)t * L + c * 8;
-                    for (int p = 1; p < P; ++p) {
-                        float x[8];
-                        lt_unpack8(lt_load16(p0 + (int64_t)p * pstride), x);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
-                    }
-                    sv[tt][i] = lt_pack8(s);
-                    lt_unpack8(sv[tt][i], s);
-                }
-                ss[tt] = lt_ss_chunk(s, ss[tt]);
-            }
-        }
-    }
-
-    // 3. RMSNorm: slots -> lanes (xor 16, xor 32) -> waves, fixed tree
-    if (norm_w) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            float v = ss[tt];
-            v = v + __shfl_xor(v, 16);
-            v = v + __shfl_xor(v, 32);
-            if (g == 0) red_ss[w][16 * tt + r] = v;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const int x = 16 * tt + r;
-            const float total = (red_ss[0][x] + red_ss[1][x]) + (red_ss[2][x] + red_ss[3][x]);
-            const float rs = lt_inv_rms(total, inv_L, eps);
+        for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                float s[8];
-                lt_unpack8(sv[tt][i], s);
-                sv[tt][i] = lt_scale_chunk(s, rs, wv[i]);
+                const int c = 4 * KW * i + 4 * w + g;
+                const uint32_t off =
+                    c < nchunk ? (uint32_t)((16 * jt + r) * L + c * 8) * 2u : LT_OOB;
+                wa[jt][i] = lt_buf_load16(rw, off);
             }
+    }
+    // this wave's epilogue fragment (w < JT*TT): token tile w % TT, row tile w / TT
+    const bool has_epi = w < JT * TT;
+    const int tte = w % TT, jte = w / TT;
+    const int te = 16 * tte + r, jl = 16 * jte + 4 * g;   // token, local row
+    const bool out_vec = has_epi && te < T && vec8 && jl + 4 <= rows;
+    u32x2_t opre = {0u, 0u};
+    if (out_vec) opre = *reinterpret_cast<const u32x2_t *>(outn + (int64_t)te * ld_out + j0 + jl);
+
+    // 2. RMSNorm (its barrier waits for LDS only; W stays in flight)
+    if (norm_w) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) latent_norm(sv[tt], wv, eps, inv_L, red_ss[tt]);
+    }
+
+    // 3. projection on the matrix cores: D[j][t] += W[j][k] * y[t][k]
+    f32x4_t acc[JT][TT];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) acc[jt][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, wa[jt][i]);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                acc[jt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a, __builtin_bit_cast(bf16x8_t, sv[tt][i]), acc[jt][tt], 0, 0, 0);
         }
-    }
 
-    // 4. projection on the matrix cores: D[j][t] += W[j][k] * y[t][k]
-    f32x4_t acc[TT];
+    // 4. add the KW waves' partial products in wave order, beta-add the window
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, wa[i]);
+        for (int tt = 0; tt < TT; ++tt) red_acc[w][jt * TT + tt][l] = acc[jt][tt];
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));   // LDS only: the out values may still fly
+    lt_lds_barrier();
+    if (!has_epi || te >= T) return;
+    f32x4_t d = red_acc[0][w][l];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, __builtin_bit_cast(bf16x8_t, sv[tt][i]), acc[tt], 0, 0, 0);
-    }
-
-    // 5. add the four waves' partial products, then beta-add onto the window
+    for (int v = 1; v < KW; ++v) d = d + red_acc[v][w][l];
+    u16 *o = outn + (int64_t)te * ld_out + j0 + jl;   // D column = lane % 16 (token),
+    if (out_vec) {                                  // rows 4*(lane/16) + 0..3 (columns)
+        u32x2_t nv;
+        nv[0] = lt_pack2(lt_bf_lo(opre[0]) + d[0], lt_bf_hi(opre[0]) + d[1]);
+        nv[1] = lt_pack2(lt_bf_lo(opre[1]) + d[2], lt_bf_hi(opre[1]) + d[3]);
+        *reinterpret_cast<u32x2_t *>(o) = nv;
+    } else {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) red_acc[w][tt][l] = acc[tt];
-    __syncthreads();
-    for (int tt = w; tt < TT; tt += 4) {
-        const f32x4_t a0 = red_acc[0][tt][l], a1 = red_acc[1][tt][l];
-        const f32x4_t a2 = red_acc[2][tt][l], a3 = red_acc[3][tt][l];
-        const f32x4_t d = (a0 + a1) + (a2 + a3);
-        const int t = 16 * tt + r;       // D column = lane % 16
-        const int j = j0 + 4 * g;        // D rows 4*(lane/16) + 0..3
-        if (t >= T) continue;
-        u16 *o = outn + (int64_t)t * ld_out + j;
-        if (vec8 && j + 4 <= n) {
-            u32x2_t ov = *reinterpret_cast<const u32x2_t *>(o);
-            u32x2_t nv;
-            nv[0] = lt_pack2(lt_bf_lo(ov[0]) + d[0], lt_bf_hi(ov[0]) + d[1]);
-            nv[1] = lt_pack2(lt_bf_lo(ov[1]) + d[2], lt_bf_hi(ov[1]) + d[3]);
-            *reinterpret_cast<u32x2_t *>(o) = nv;
-        } else {
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                if (j + a < n) {
-                    const float v = lt_bf_lo((uint32_t)o[a]) + d[a];
-                    o[a] = (u16)(lt_pack2(v, 0.f) & 0xFFFFu);
-                }
+        for (int a = 0; a < 4; ++a) {
+            if (jl + a < rows) {
+                const float v = lt_bf_lo((uint32_t)o[a]) + d[a];
+                o[a] = (u16)(lt_pack2(v, 0.f) & 0xFFFFu);
             }
         }
     }
 }
 
-template <int NI, int TT>
+// Rows of the window per workgroup: about one block per compute unit, a
+// multiple of 4 (the epilogue's column group), at most 32 (two MFMA tiles).
+int rows_per_block(int n)
+{
+    constexpr int CUS = 256;
+    const int rw = ((n + CUS - 1) / CUS + 3) / 4 * 4;
+    return rw < 4 ? 4 : (rw > 32 ? 32 : rw);
+}
+
+template <int NI, int TT, int JT>
 hipError_t launch_nt(const u16 *part, int64_t pstride, int P, int T, int L, const u16 *norm_w,
-                     float eps, const u16 *Wn, int n, u16 *outn, int64_t ld_out, int vec8,
+                     float eps, const u16 *Wn, int n, int RW, u16 *outn, int64_t ld_out, int vec8,
                      hipStream_t stream)
 {
-    const dim3 grid((n + 15) / 16), block(256);
-    hipLaunchKernelGGL((k_skinny<NI, TT>), grid, block, 0, stream, part, pstride, P, T, L,
-                       norm_w, eps, 1.0f / (float)L, Wn, n, outn, ld_out, vec8);
+    const dim3 grid((n + RW - 1) / RW), block(64 * KW);
+    hipLaunchKernelGGL((k_skinny<NI, TT, JT>), grid, block, 0, stream, part, pstride, P, T, L,
+                       norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8);
     return hipGetLastError();
+}
+
+template <int NI, int JT>
+hipError_t launch_jt(const u16 *part, int64_t pstride, int P, int T, int L, const u16 *norm_w,
+                     float eps, const u16 *Wn, int n, int RW, u16 *outn, int64_t ld_out, int vec8,
+                     hipStream_t stream)
+{
+    if (T <= 16)
+        return launch_nt<NI, 1, JT>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out,
+                                    vec8, stream);
+    if (T <= 32)
+        return launch_nt<NI, 2, JT>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out,
+                                    vec8, stream);
+    if constexpr (NI <= 4)
+        return launch_nt<NI, 4, JT>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out,
+                                    vec8, stream);
+    return hipErrorInvalidValue;
 }
 
 template <int NI>
@@ -188,22 +180,17 @@ hipError_t launch_ni(const u16 *part, int64_t pstride, int P, int T, int L, cons
                      float eps, const u16 *Wn, int n, u16 *outn, int64_t ld_out, int vec8,
                      hipStream_t stream)
 {
-    if (T <= 16)
-        return launch_nt<NI, 1>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8,
-                                stream);
-    if constexpr (NI <= 8) {
-        if (T <= 32)
-            return launch_nt<NI, 2>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out,
-                                    vec8, stream);
-        return launch_nt<NI, 4>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8,
-                                stream);
-    }
-    return hipErrorInvalidValue;
+    const int RW = rows_per_block(n);
+    if (RW <= 16)
+        return launch_jt<NI, 1>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out,
+                                vec8, stream);
+    return launch_jt<NI, 2>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out, vec8,
+                            stream);
 }
 
 }  // namespace
 
-int skinny_tokens_per_launch(int L) { return L > 1024 ? 16 : 64; }
+int skinny_tokens_per_launch(int L) { return latent_steps(L) > 4 ? 32 : 64; }
 
 hipError_t launch_skinny(const uint16_t *part, int64_t pstride, int P, int T, int L,
                          const uint16_t *norm_w, float eps, const uint16_t *Wn, int n,
@@ -211,12 +198,11 @@ hipError_t launch_skinny(const uint16_t *part, int64_t pstride, int P, int T, in
 {
     if (T < 1 || T > skinny_tokens_per_launch(L)) return hipErrorInvalidValue;
     const int vec8 = ((reinterpret_cast<uintptr_t>(outn) & 7) == 0) && (ld_out % 4 == 0);
-    const int ni = (L + 127) / 128;
+    const int ni = latent_steps(L);
     if (ni <= 1) return launch_ni<1>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
     if (ni <= 2) return launch_ni<2>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
     if (ni <= 4) return launch_ni<4>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
-    if (ni <= 8) return launch_ni<8>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
-    return launch_ni<16>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
+    return launch_ni<8>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
 }
 
 }  // namespace lt

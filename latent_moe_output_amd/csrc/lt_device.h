@@ -1,10 +1,7 @@
 // lt_device.h -- device-side helpers shared by the tail's HIP kernels.
 //
-// Holds the vector types, bf16 conversions and the one definition of how a
-// latent row is reduced and normalised.  Both the weight-streaming kernel and
-// the sum+RMSNorm kernel build their latent from these helpers with the same
-// assignment of 8-element chunks to reduction slots, so the two paths produce
-// bit-identical latents for the same inputs.
+// Vector types, bf16 conversions, the RMSNorm scaling step and the LDS
+// hand-off barrier.  How a latent tile is built lives in lt_latent.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,9 +18,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // One 8-element chunk (16 bytes) of a bf16 row.
 #define LT_CHUNK 8
-// Chunks of a row are dealt round-robin to 16 reduction slots: chunk c goes to
-// slot c % 16 and is that slot's (c / 16)-th term.
-#define LT_SLOTS 16
 
 __device__ __forceinline__ float lt_bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float lt_bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -58,36 +52,21 @@ __device__ __forceinline__ u32x4_t lt_load16(const u16 *p)
     return *reinterpret_cast<const u32x4_t *>(p);
 }
 
-// Sum of the P partial chunks starting at `p0` (partial stride `pstride`
-// elements), fp32, p ascending; with more than one partial the sum is rounded
-// to bf16 (the reduced latent is stored as bf16 before it is normalised).
-// Returns the chunk as packed bf16 and its float values in s[8].
-__device__ __forceinline__ u32x4_t lt_sum_chunk(const u16 *p0, int64_t pstride, int P,
-                                                float s[8])
+// Raw buffer resources (stride 0): a load whose byte offset is at or past
+// num_records returns zeros, so ragged edges need no branches.
+constexpr uint32_t LT_RSRC_W3 = 0x00020000u;   // raw buffer, dword data
+constexpr uint32_t LT_OOB = 0x80000000u;       // an offset every resource rejects
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lt_rsrc(const void *base, uint32_t bytes)
 {
-    u32x4_t v = lt_load16(p0);
-    if (P == 1) {
-        lt_unpack8(v, s);
-        return v;
-    }
-    lt_unpack8(v, s);
-    for (int p = 1; p < P; ++p) {
-        float x[8];
-        lt_unpack8(lt_load16(p0 + (int64_t)p * pstride), x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
-    }
-    u32x4_t r = lt_pack8(s);
-    lt_unpack8(r, s);
-    return r;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             LT_RSRC_W3);
 }
 
-// Adds the squares of one chunk to a slot's running sum, elements in order.
-__device__ __forceinline__ float lt_ss_chunk(const float s[8], float acc)
+// 16-byte load at byte offset `off` of a resource (zeros when out of range).
+__device__ __forceinline__ u32x4_t lt_buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(s[e], s[e], acc);
-    return acc;
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 // 1 / sqrt(mean square + eps) from the row's total of squares.
@@ -106,5 +85,19 @@ __device__ __forceinline__ u32x4_t lt_scale_chunk(const float s[8], float r, u32
     return lt_pack8(y);
 }
 
-// The 16 slot sums of a row are combined as a balanced binary tree in slot
-// order: ((S0+S1)+(S2+S3)) + ((S4+S5)+(S6+S7)) + ...  Both kernels follow it.
+// s_waitcnt immediate (gfx9 encoding): wait until at most `n` vector memory
+// operations are outstanding and all LDS operations have completed.
+constexpr int lt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
+
+// Workgroup barrier for LDS hand-offs.  The caller has already waited (with
+// s_waitcnt) for exactly the loads and LDS operations the hand-off needs;
+// __syncthreads() would add a release fence that drains every outstanding
+// global load, including loads meant to stay in flight across the barrier.
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lt_lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}

@@ -1,0 +1,134 @@
+// lt_latent.h -- the one definition of how a 16-token tile's latent is built.
+//
+// Partial sum, bf16 storage round trip and RMSNorm
+// ([PR51253 Key source snippets, `_check_matches_replicated`]: reduce the
+// routed partials first, then `F.rms_norm` over the latent width with the
+// norm weight and eps; [PR50593 Implementation, item 1]: fp32 accumulation,
+// bf16 storage round trip, fp32 variance).
+//
+// A workgroup of KW waves computes the latent of 16 tokens directly in the
+// B-operand register layout of v_mfma_f32_16x16x32_bf16: at step i, lane l of
+// wave w holds chunk c = 4*KW*i + 4*w + (l >> 4) (latent elements 8c..8c+7)
+// of token (l & 15).  Both the weight-streaming kernel (which multiplies the
+// registers straight away) and the sum+RMSNorm kernel (which stores them)
+// build their latent with these functions and the same KW, so the two paths
+// give bit-identical latents.
+//
+// The sum of squares of each token is taken on the matrix cores: with the
+// tile S in both operand slots, v_mfma_f32_16x16x32_bf16 accumulates S * S^T,
+// whose diagonal holds each token's sum of squares over the wave's chunks.
+// The KW per-wave sums are then added in wave order through LDS.
+#pragma once
+
+#include "lt_device.h"
+
+namespace lt {
+
+constexpr int KW = 8;   // waves splitting the latent width
+
+// Steps needed for latent width L (chunks of 8, 4*KW chunks per step).
+__host__ __device__ constexpr int latent_steps(int L) { return (L + 32 * KW - 1) / (32 * KW); }
+
+// Byte offset of this lane's chunk at step i within a tile of row stride L,
+// or LT_OOB past the row end.
+__device__ __forceinline__ uint32_t latent_offset(int i, int L)
+{
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = 4 * KW * i + 4 * w + (l >> 4);
+    return c < (L >> 3) ? (uint32_t)((l & 15) * L + c * 8) * 2u : LT_OOB;
+}
+
+// Bytes of a tile holding Tv valid token rows (none when Tv <= 0).
+__device__ __forceinline__ uint32_t latent_tile_bytes(int Tv, int L)
+{
+    return Tv > 0 ? (uint32_t)(Tv * L) * 2u : 0u;
+}
+
+// Loads partial 0 of this lane's chunks of tokens [0, Tv) of the tile whose
+// first token row starts at `tile` (row stride L).  Chunks past the row end
+// and tokens >= Tv read as zero (buffer range check, no branches).
+template <int NI>
+__device__ __forceinline__ void latent_load(const u16 *__restrict__ tile, int Tv, int L,
+                                            u32x4_t (&sv)[NI])
+{
+    const __amdgpu_buffer_rsrc_t r = lt_rsrc(tile, latent_tile_bytes(Tv, L));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) sv[i] = lt_buf_load16(r, latent_offset(i, L));
+}
+
+// Loads this lane's chunks of the norm weight (zeros past the row end).
+template <int NI>
+__device__ __forceinline__ void latent_load_weight(const u16 *__restrict__ norm_w, int L,
+                                                   u32x4_t (&wv)[NI])
+{
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = l >> 4;
+    const __amdgpu_buffer_rsrc_t r = lt_rsrc(norm_w, (uint32_t)L * 2u);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        wv[i] = lt_buf_load16(r, (uint32_t)(4 * KW * i + 4 * w + g) * 16u);
+}
+
+// Adds partials 1..P-1 (stride pstride elements) in fp32, p ascending, and
+// stores the sum as bf16.  Nothing to do for one partial.  Each partial's
+// NI chunks are loaded together, so a pass costs one memory round trip.
+template <int NI>
+__device__ __forceinline__ void latent_sum(const u16 *__restrict__ tile, int64_t pstride, int P,
+                                           int Tv, int L, u32x4_t (&sv)[NI])
+{
+    if (P <= 1) return;
+    uint32_t off[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) off[i] = latent_offset(i, L);
+    float s[NI][8];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) lt_unpack8(sv[i], s[i]);
+    for (int p = 1; p < P; ++p) {
+        const __amdgpu_buffer_rsrc_t r = lt_rsrc(tile + (int64_t)p * pstride, latent_tile_bytes(Tv, L));
+        u32x4_t x[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) x[i] = lt_buf_load16(r, off[i]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float f[8];
+            lt_unpack8(x[i], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[i][e] = s[i][e] + f[e];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) sv[i] = lt_pack8(s[i]);
+}
+
+// RMSNorm of the tile in place: y = bf16((s * rsqrt(mean(s^2) + eps)) * w).
+// `red` is LDS scratch of KW * 16 floats.  Contains a workgroup barrier:
+// every thread of the workgroup must call it.
+template <int NI>
+__device__ __forceinline__ void latent_norm(u32x4_t (&sv)[NI], const u32x4_t (&wv)[NI],
+                                            float eps, float inv_L, float *red)
+{
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = l & 15;
+    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const bf16x8_t s = __builtin_bit_cast(bf16x8_t, sv[i]);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s, s, d, 0, 0, 0);
+    }
+    // D[t][t] sits in lane 16*(t/4) + t, element t % 4
+    if ((l >> 4) == (t >> 2)) red[w * 16 + t] = d[t & 3];
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));   // LDS only: loads may stay in flight
+    lt_lds_barrier();
+    float total = red[t];
+#pragma unroll
+    for (int v = 1; v < KW; ++v) total = total + red[v * 16 + t];
+    const float rs = lt_inv_rms(total, inv_L, eps);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        float s[8];
+        lt_unpack8(sv[i], s);
+        sv[i] = lt_scale_chunk(s, rs, wv[i]);
+    }
+}
+
+}  // namespace lt

@@ -260,6 +260,20 @@ def test_edge_shapes(T, L, H, P, c0, n, ld):
     assert_window_close(got, ref, c0, n, "edge T=%d L=%d" % (T, L))
 
 
+@pytest.mark.parametrize("T", [1, 17, 33, 64])
+@pytest.mark.parametrize("n,L", [(7168, 1024), (7100, 1024), (5000, 264), (4097, 1024),
+                                 (9000, 520), (12, 1024)])
+def test_skinny_row_blocks(T, n, L, forced):
+    """Weight-streaming path over window widths whose row blocks (4..32 rows,
+    one or two MFMA tiles, a short last block) cover every epilogue case."""
+    forced(64)
+    wl = synth.Workload("rowblk", T=T, L=L, H=n + 11, P=2, c0=5, n=n, ld_out=n + 13,
+                        part_std=0.6)
+    assert binding.lt_path_for(T, n) == 1
+    _, got, ref = _run_full(wl, seed=T * 7 + n)
+    assert_window_close(got, ref, 5, n, "rowblk T=%d n=%d L=%d" % (T, n, L))
+
+
 def test_sentinels_outside_window_survive():
     """NaN payloads, -0.0 and +-9984 outside the window and in the padding."""
     from oracle import oracle
