@@ -23,7 +23,9 @@ benchmark stream around each call and, through lt_set_kernel_events, around
 its projection kernel.  `roofline` is for the dominant kernel (k_gemm at
 T=8192); `roofline_skinny` for the weight-streaming kernel at T <= 16;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the T=8192
-call on this host's cores.
+call on this host's cores.  `roofline.traffic` is the GEMM's HBM bytes per
+launch from the committed rocprofv3 counter summary under profiles/, or null
+once the GEMM sources differ from the ones those counters were taken on.
 """
 from __future__ import annotations
 
@@ -95,6 +97,31 @@ class Hip:
 
     def destroy(self, ev):
         self.lib.hipEventDestroy(ev)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_tsweep_L1024_H7168_hbm_traffic.md")
+GEMM_SOURCES = [os.path.join(ROOT, "latent_moe_output_amd", "csrc", f)
+                for f in ("k_gemm.hip", "lt_device.h")]
+
+
+def gemm_traffic_bytes():
+    """HBM bytes per launch of the T=8192 GEMM from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled against a plain copy), or None
+    when the GEMM sources changed since the counters were taken."""
+    import hashlib
+
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = b"".join(open(f, "rb").read() for f in GEMM_SOURCES)
+    except OSError:
+        return None
+    sha = hashlib.sha256(src).hexdigest()
+    for line in text.splitlines():
+        if line.startswith("traffic_k_gemm_T8192 "):
+            kv = dict(x.split("=", 1) for x in line.split()[1:])
+            if kv.get("sources_sha256") == sha:
+                return int(kv["bytes"])
+    return None
 
 
 def cpu_baseline(d, target_s=12.0):
@@ -253,8 +280,8 @@ def main():
         "peak": MFMA_BF16_PEAK / 1e12,
         "unit": "TFLOP/s",
         "frac": round(g_ach / MFMA_BF16_PEAK, 4),
-        "traffic": None,
-        "kernel": "k_gemm<256,256> (T=8192, L=1024, n=7168)",
+        "traffic": gemm_traffic_bytes(),
+        "kernel": "k_gemm, 256x256 tiles (T=8192, L=1024, n=7168)",
         "avg_launch_us": round(kern_us[Tg], 3),
         "flops_per_launch": flops_of(Tg),
     }
@@ -268,7 +295,7 @@ def main():
         "unit": "GB/s",
         "frac": round(sk_bytes / (sk_us * 1e-6) / HBM_PEAK, 4),
         "traffic": None,
-        "kernel": "k_skinny<8,1> (T=1,2,4,8,16; L=1024, n=7168)",
+        "kernel": "k_skinny, one 16-token tile (T=1,2,4,8,16; L=1024, n=7168)",
         "avg_launch_us": round(sk_us / len(sk), 3),
         "bytes_per_launch_avg": sk_bytes // len(sk),
     }
