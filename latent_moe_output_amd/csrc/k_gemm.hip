@@ -428,13 +428,14 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
                        uint16_t *outn, int64_t ld_out, hipStream_t stream)
 {
     const bool vec16 = ((reinterpret_cast<uintptr_t>(outn) & 15) == 0) && (ld_out % 8 == 0);
-    const int64_t tiles256 = (int64_t)((n + 255) / 256) * ((T + 255) / 256);
+    // Tile shape by tile count (measured on n = 7168, T = 128 .. 8192): 128 x 128
+    // tiles run two workgroups per CU, which hide each other's barriers and
+    // epilogues, and beat 256 x 256 tiles even at T = 8192; below about 224 of
+    // them, 64 (columns) x 128 (tokens) tiles keep the CUs busy.
     const int64_t tiles128 = (int64_t)((n + 127) / 128) * ((T + 127) / 128);
-    if (tiles256 >= 512)
-        return launch_cfg<256, 256, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
-    if (tiles128 >= 256)
+    if (tiles128 >= 224)
         return launch_cfg<128, 128, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
-    return launch_cfg<64, 64, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+    return launch_cfg<64, 128, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
 }
 
 }  // namespace lt
