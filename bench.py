@@ -281,7 +281,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(g_ach / MFMA_BF16_PEAK, 4),
         "traffic": gemm_traffic_bytes(),
-        "kernel": "k_gemm, 128x128 tiles (T=8192, L=1024, n=7168)",
+        "kernel": "k_gemm, 256x256 tiles, 8 waves (T=8192, L=1024, n=7168)",
         "avg_launch_us": round(kern_us[Tg], 3),
         "flops_per_launch": flops_of(Tg),
     }

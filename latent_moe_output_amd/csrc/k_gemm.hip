@@ -7,8 +7,8 @@
 // projection instead of running a separate add.
 //
 // Layout on gfx950:
-//  * Workgroup tile BJ (W rows = output columns) x BT (tokens), 4 waves in a
-//    2 x 2 grid.  Each wave owns (BJ/2) x (BT/2) as 32 x 32 tiles of
+//  * Workgroup tile BJ (W rows = output columns) x BT (tokens), WGJ x WGT
+//    waves.  Each wave owns (BJ/WGJ) x (BT/WGT) as 32 x 32 tiles of
 //    v_mfma_f32_32x32x16_bf16 with W as the A operand and the latent as B.
 //  * K advances 32 at a time through NS = 4 LDS stages filled straight from
 //    HBM/L2 by buffer_load_dwordx4 ... lds, so three stages are in flight
@@ -67,14 +67,18 @@ __device__ __forceinline__ int perm32(int m)
 // conflicts on gfx950 (measured); both operands are read that way.
 __device__ __forceinline__ int swz(int r) { return (((r >> 3) & 1) << 1) | (((r >> 1) ^ (r >> 2)) & 1); }
 
-template <int BJ, int BT, int GROUP_J, bool KTAIL, bool EPI_LDS>
-__global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t T, int L,
+template <int BJ, int BT, int WGJ, int WGT, int GROUP_J, bool KTAIL, bool EPI_LDS>
+__global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__ Y, int64_t T, int L,
                                               const u16 *__restrict__ Wn, int n,
                                               u16 *__restrict__ outn, int64_t ld_out, int ntj,
                                               int ntt)
 {
-    constexpr int MJ = BJ / 64, MT = BT / 64;   // 32x32 tiles per wave
-    constexpr int LA = BJ / 64, LB = BT / 64;   // direct loads per thread per stage
+    constexpr int NW = WGJ * WGT;               // waves, in a WGJ x WGT grid
+    constexpr int NT = 64 * NW;                 // threads
+    constexpr int MJ = BJ / WGJ / 32, MT = BT / WGT / 32;   // 32x32 tiles per wave
+    constexpr int LR = 16 * NW;                 // stage rows one direct load fills
+    constexpr int LA = BJ / LR, LB = BT / LR;   // direct loads per thread per stage
+    static_assert(MJ >= 1 && MT >= 1 && LA * LR == BJ && LB * LR == BT, "tile shape");
     constexpr int LPS = LA + LB;
     constexpr int STAGE_A = BJ * ROWB, STAGE = (BJ + BT) * ROWB;
     constexpr int NFR = MJ + MT, NMF = MJ * MT;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wj = w >> 1, wt = w & 1;
+    const int wj = w / WGT, wt = w % WGT;
     const int nchunk = L >> 3;
     // K steps, padded to whole trips of NS steps; padded steps read zeros
     // (KTAIL masking), so every trip has the same straight-line body.
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(Y + t0 * L), (short)0, (int)((uint32_t)rows_b * row_bytes), RSRC_W3);
 
-    // ---- direct loads: lane i of wave w, load q -> stage row 64q + 16w + i/4,
+    // ---- direct loads: lane i of wave w, load q -> stage row LR*q + 16w + i/4,
     // LDS slot i%4, global chunk (slot ^ key(row)).
     const int lrow = 16 * w + (l >> 2);
     const int lslot = l & 3;
@@ -136,13 +140,13 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
     int cha[LA], chb[LB];
 #pragma unroll
     for (int q = 0; q < LA; ++q) {
-        const int row = 64 * q + lrow;
+        const int row = LR * q + lrow;
         cha[q] = lslot ^ swz(row);
         offa[q] = (uint32_t)row * row_bytes + (uint32_t)cha[q] * 16u;
     }
 #pragma unroll
     for (int q = 0; q < LB; ++q) {
-        const int row = 64 * q + lrow;
+        const int row = LR * q + lrow;
         chb[q] = lslot ^ swz(row);
         offb[q] = (uint32_t)row * row_bytes + (uint32_t)chb[q] * 16u;
     }
@@ -154,22 +158,22 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
         for (int q = 0; q < LA; ++q) {
             uint32_t vo = offa[q] + kbyte;
             if (KTAIL && s * 4 + cha[q] >= nchunk) vo = OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (64 * q + 16 * w) * ROWB),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (LR * q + 16 * w) * ROWB),
                                                      16, vo, 0, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < LB; ++q) {
             uint32_t vo = offb[q] + kbyte;
             if (KTAIL && s * 4 + chb[q] >= nchunk) vo = OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + (64 * q + 16 * w) * ROWB),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + (LR * q + 16 * w) * ROWB),
                                                      16, vo, 0, 0, 0);
         }
     };
 
     // ---- fragment reads (byte offsets within a stage)
     const int hsel = l >> 5;
-    const int arow = wj * (BJ / 2) + perm32(l & 31);
-    const int brow = wt * (BT / 2) + perm32(l & 31);   // token of this lane's D column
+    const int arow = wj * (BJ / WGJ) + perm32(l & 31);
+    const int brow = wt * (BT / WGT) + perm32(l & 31);   // token of this lane's D column
     int afr[2], bfr[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -208,15 +212,15 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
     constexpr int CPRE = BJ / 8;               // 16-byte chunks per tile row
     constexpr int RPQ = BT / 4;                // tile rows per quarter
     constexpr int QCH = RPQ * CPRE;            // chunks per quarter
-    constexpr int QLD = QCH / 256;             // direct loads per thread per quarter
-    static_assert(!EPI_LDS || QCH % 256 == 0, "a quarter is whole workgroup loads");
+    constexpr int QLD = QCH / NT;              // direct loads per thread per quarter
+    static_assert(!EPI_LDS || QCH % NT == 0, "a quarter is whole workgroup loads");
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(outn + t0 * ld_out), (short)0,
         (int)(((int64_t)max(rows_b - 1, 0) * ld_out + n) * 2), RSRC_W3);
     auto load_c_quarter = [&](char *dst, int q) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < QLD; ++it) {
-            const int idx0 = it * 256 + 64 * w;     // wave-uniform
+            const int idx0 = it * NT + 64 * w;      // wave-uniform
             const int idx = idx0 + l;
             const int r = q * RPQ + idx / CPRE;
             const int c = (idx % CPRE) ^ (r & (CPRE - 1));
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
             for (int mj = 0; mj < MJ; ++mj) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    const int c = (wj * (BJ / 2) + 32 * mj + 16 * half + 8 * hsel) >> 3;
+                    const int c = (wj * (BJ / WGJ) + 32 * mj + 16 * half + 8 * hsel) >> 3;
                     const f32x16_t &a = acc[mj][mt];
                     u32x4_t *ptr = reinterpret_cast<u32x4_t *>(stage_row(r) +
                                                                ((c ^ (r & (CPRE - 1))) << 4));
@@ -345,7 +349,8 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
         // ---- write back whole row segments
         constexpr int LPR = CPRE;                     // lanes per tile row
         constexpr int RPI = 64 / LPR;                 // rows per store instruction
-        constexpr int ROWS_W = BT / 4;                // rows per wave
+        constexpr int ROWS_W = BT / NW;               // rows per wave
+        static_assert(ROWS_W % RPI == 0, "whole store rounds per wave");
         static_assert(CPRE <= 64, "row wider than a wave");
 #pragma unroll 4
         for (int i = 0; i < ROWS_W / RPI; ++i) {
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
             for (int mj = 0; mj < MJ; ++mj) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    const int j = j0 + wj * (BJ / 2) + 32 * mj + 16 * half + 8 * hsel;
+                    const int j = j0 + wj * (BJ / WGJ) + 32 * mj + 16 * half + 8 * hsel;
                     const f32x16_t &a = acc[mj][mt];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -393,22 +398,22 @@ __global__ __launch_bounds__(256) void k_gemm(const u16 *__restrict__ Y, int64_t
     }
 }
 
-template <int BJ, int BT, int GROUP_J>
+template <int BJ, int BT, int WGJ, int WGT, int GROUP_J>
 hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 *outn,
                       int64_t ld_out, bool vec16, hipStream_t stream)
 {
     const int ntj = (n + BJ - 1) / BJ;
     const int64_t ntt = (T + BT - 1) / BT;
     if ((int64_t)ntj * ntt > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(ntj * ntt)), block(256);
+    const dim3 grid((unsigned)(ntj * ntt)), block(64 * WGJ * WGT);
     // The LDS epilogue moves whole out-tile quarters with workgroup-wide 16-byte
     // direct loads and addresses `out` through 32-bit buffer offsets: it needs
     // an aligned window and a tile extent below 2 GiB; anything else (and tiles
     // too small for whole-workgroup quarters) takes the plain epilogue.
-    constexpr bool EPI_OK = ((BT / 4) * (BJ / 8)) % 256 == 0;
+    constexpr bool EPI_OK = ((BT / 4) * (BJ / 8)) % (64 * WGJ * WGT) == 0;
     const bool epi = EPI_OK && vec16 && (int64_t)BT * ld_out * 2 < ((int64_t)1 << 31);
 #define LT_GEMM_LAUNCH(KT, EPI)                                                              \
-    hipLaunchKernelGGL((k_gemm<BJ, BT, GROUP_J, KT, EPI>), grid, block, 0, stream, y, T, L, Wn, \
+    hipLaunchKernelGGL((k_gemm<BJ, BT, WGJ, WGT, GROUP_J, KT, EPI>), grid, block, 0, stream, y, T, L, Wn, \
                        n, outn, ld_out, ntj, (int)ntt)
     const bool kt = L % (BK * NS) != 0;
     if constexpr (EPI_OK) {
@@ -428,14 +433,18 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
                        uint16_t *outn, int64_t ld_out, hipStream_t stream)
 {
     const bool vec16 = ((reinterpret_cast<uintptr_t>(outn) & 15) == 0) && (ld_out % 8 == 0);
-    // Tile shape by tile count (measured on n = 7168, T = 128 .. 8192): 128 x 128
-    // tiles run two workgroups per CU, which hide each other's barriers and
-    // epilogues, and beat 256 x 256 tiles even at T = 8192; below about 224 of
-    // them, 64 (columns) x 128 (tokens) tiles keep the CUs busy.
-    const int64_t tiles128 = (int64_t)((n + 127) / 128) * ((T + 127) / 128);
-    if (tiles128 >= 224)
-        return launch_cfg<128, 128, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
-    return launch_cfg<64, 128, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+    // Tile shape by tile count (measured on n = 7168, T = 128 .. 8192): the
+    // largest tile that still gives about one tile per CU.  The big tiles run
+    // 8 waves (two per SIMD, which hide each other's LDS and barrier waits);
+    // the 64 x 128 tile runs 4 waves and three workgroups per CU.
+    auto tiles = [&](int bj, int bt) { return (int64_t)((n + bj - 1) / bj) * ((T + bt - 1) / bt); };
+    if (tiles(256, 256) >= 224)
+        return launch_cfg<256, 256, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+    if (tiles(128, 256) >= 224)
+        return launch_cfg<128, 256, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+    if (tiles(128, 128) >= 224)
+        return launch_cfg<128, 128, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+    return launch_cfg<64, 128, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
 }
 
 }  // namespace lt

@@ -108,6 +108,36 @@ def test_large_workload_sampled(name):
     assert np.array_equal(got[outside], d["out"][outside])
 
 
+@pytest.mark.parametrize("T,n,c0,ld,P", [
+    (2000, 7100, 37, 7168, 2),   # 256 x 256 tiles, 8 waves (224 tiles), ragged both ways
+    (1000, 7100, 5, 7120, 1),    # 128 x 256 tiles, 8 waves
+    (500, 7100, 11, 7128, 3),    # 128 x 128 tiles, 8 waves
+    (300, 3000, 8, 3016, 1),     # 64 x 128 tiles, 4 waves
+])
+def test_gemm_tile_shapes_sampled(T, n, c0, ld, P):
+    """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
+    offset window: oracle on sampled rows (tile edges included, all window
+    columns), untouched elements over the whole buffer."""
+    from oracle import oracle
+
+    wl = synth.Workload("tiles", T=T, L=1024, H=c0 + n + 3, P=P, c0=c0, n=n, ld_out=ld,
+                        part_std=0.6)
+    d = synth.generate(wl, seed=T + n)
+    di = DevInputs(d)
+    say("case tiles T=%d n=%d c0=%d ld=%d P=%d" % (T, n, c0, ld, P))
+    assert binding.lt_path_for(T, n) == 2
+    binding.check(di.call(wl))
+    _sync()
+    got = host(di.out)
+    rows = sample_rows(T, k=24, seed=2)
+    ref = oracle.latent_tail(d["partials"][:, rows, :], d["norm_w"], eps32(wl), d["W"], c0, n,
+                             d["out"][rows])
+    assert_window_close(got[rows], ref, c0, n, "tiles T=%d n=%d" % (T, n))
+    outside = np.ones(got.shape, dtype=bool)
+    outside[:, c0:c0 + n] = False
+    assert np.array_equal(got[outside], d["out"][outside])
+
+
 # --------------------------------------------------------------------------
 # dispatch boundary and forced paths
 # --------------------------------------------------------------------------
