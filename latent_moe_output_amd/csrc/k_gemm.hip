@@ -10,32 +10,36 @@
 //  * Workgroup tile BJ (W rows = output columns) x BT (tokens), WGJ x WGT
 //    waves.  Each wave owns (BJ/WGJ) x (BT/WGT) as 32 x 32 tiles of
 //    v_mfma_f32_32x32x16_bf16 with W as the A operand and the latent as B.
-//  * K advances 32 at a time through NS = 4 LDS stages filled straight from
-//    HBM/L2 by buffer_load_dwordx4 ... lds, so three stages are in flight
-//    while one is multiplied.  Buffer resources are clipped per workgroup:
-//    rows past the end of W's window or past T read as zero with no branch.
-//  * A stage row is 32 bf16 = four 16-byte chunks; each direct load writes
-//    1 KB (16 rows) contiguously, and the chunk a lane fetches is chosen so
-//    the rows land XOR-swizzled.  Fragments of both operands are read from
-//    rows perm32(lane % 32) of each 32-row block, which with the XOR key is
-//    free of bank conflicts (so the latent's token order inside a block is
-//    permuted the same way; the epilogue follows it).
-//  * One barrier per K step, placed between the step's two MFMA halves: the
-//    second half's fragments are read before it and the next step's first
-//    fragments right after it, so LDS latency hides behind MFMA work.
-//  * A-operand rows are read through a fixed permutation of the 32 rows of a
-//    tile so that each lane holds 16 consecutive output columns (two runs of
-//    8).  The `out` tile is read in that layout with 16-byte loads during the
-//    last three K steps; the sums are rounded, staged in LDS (swizzled) and
-//    written back row by row, so every store instruction covers whole
-//    contiguous row segments of `out`.
+//  * K advances 64 at a time through NS (2 or 4) LDS stages filled straight
+//    from L2 by buffer_load_dwordx4 ... lds: while one stage is multiplied
+//    the next NS-1 are in flight.  A stage row is 64 bf16 = one whole 128-byte line of
+//    the operand row, the unit the L2 hands out; half-line slices (32 bf16)
+//    measured at half the fill rate.  Buffer resources are clipped per
+//    workgroup: rows past the end of W's window or past T read as zero with
+//    no branch.
+//  * Each direct load writes 1 KB (8 rows) contiguously; the 16-byte chunk a
+//    lane fetches is chosen so the rows land XOR-swizzled (key swz8).
+//    Fragments of both operands are read from rows perm32(lane % 32) of each
+//    32-row block, which with that key keeps every 8- and 16-lane group of a
+//    ds_read_b128 on distinct banks (so the latent's token order inside a
+//    block is permuted the same way; the epilogue follows it).
+//  * Fragments are double-buffered in registers across the four 16-wide K
+//    slices of a stage.  One barrier per stage, placed between the two MFMA
+//    halves of the last slice: the next stage's first fragments are read right
+//    after it while the second half runs.
+//  * Epilogue: the `out` tile moves through LDS in two halves of token rows,
+//    fetched into stage arrays as soon as the K loop frees them (with two
+//    stages: half 0 during the last K stage, half 1 once the MFMAs are done,
+//    while the waves owning half 0 form their sums).  Sums are rounded once in place and the tile is
+//    written back row by row, so every store covers whole contiguous row
+//    segments of `out`.
 //  * Ragged edges are masked on store; nothing outside [c0, c0+n) x [0, T) is
 //    written.
 //  * Tiles are spread so that each of the 8 XCDs receives a contiguous range
 //    of the (grouped) tile order, keeping W and latent blocks that are reused
 //    by neighbouring tiles in the same XCD's L2.
-// Each output element's accumulation order depends on (L, tile config) only,
-// not on c0 or n.
+// Each output element's accumulation order depends on L only (K ascending in
+// 16-wide MFMA slices), not on c0, n or the tile shape.
 #include <type_traits>
 
 #include "lt_device.h"
@@ -44,53 +48,54 @@
 namespace lt {
 namespace {
 
-constexpr int BK = 32;                    // K per stage
-constexpr int NS = 4;                     // LDS stages
-constexpr int ROWB = BK * 2;              // bytes per stage row
+constexpr int BK = 64;                    // K per stage
+constexpr int ROWB = BK * 2;              // bytes per stage row (one 128-byte line)
+constexpr int CPR = ROWB / 16;            // 16-byte chunks per stage row
+constexpr int KSL = BK / 16;              // 16-wide MFMA K slices per stage
 constexpr int NUM_XCD = 8;
-constexpr uint32_t RSRC_W3 = LT_RSRC_W3;
 constexpr uint32_t OOB = LT_OOB;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int V> using I = std::integral_constant<int, V>;
-template <bool V> using B = std::integral_constant<bool, V>;
 
-// Row permutation of a 32-row A tile: MFMA row m reads LDS row perm32(m).
+// Row permutation of a 32-row block: MFMA row m reads LDS row perm32(m).
 __device__ __forceinline__ int perm32(int m)
 {
     const int q = m >> 3, hh = (m >> 2) & 1, alo = m & 3;
     return 16 * (q >> 1) + 8 * hh + 4 * (q & 1) + alo;
 }
-// Chunk-slot XOR key (4 slots of 16 bytes per 64-byte stage row).  Fragment
-// reads of the 32 rows perm32(0..31) with this key are free of LDS bank
-// conflicts on gfx950 (measured); both operands are read that way.
-__device__ __forceinline__ int swz(int r) { return (((r >> 3) & 1) << 1) | (((r >> 1) ^ (r >> 2)) & 1); }
+// Chunk-slot XOR key (8 slots of 16 bytes per 128-byte stage row).  Over the
+// rows perm32(0..31) it is a permutation on every aligned group of 8 lanes and
+// on the even and the odd rows of every aligned group of 16 lanes, so
+// fragment reads hit distinct banks.
+__device__ __forceinline__ int swz8(int r)
+{
+    return ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
+}
 
-template <int BJ, int BT, int WGJ, int WGT, int GROUP_J, bool KTAIL, bool EPI_LDS>
+template <int BJ, int BT, int WGJ, int WGT, int NS, int GROUP_J, bool KTAIL, bool EPI_LDS>
 __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__ Y, int64_t T, int L,
-                                              const u16 *__restrict__ Wn, int n,
-                                              u16 *__restrict__ outn, int64_t ld_out, int ntj,
-                                              int ntt)
+                                                         const u16 *__restrict__ Wn, int n,
+                                                         u16 *__restrict__ outn, int64_t ld_out,
+                                                         int ntj, int ntt)
 {
     constexpr int NW = WGJ * WGT;               // waves, in a WGJ x WGT grid
     constexpr int NT = 64 * NW;                 // threads
     constexpr int MJ = BJ / WGJ / 32, MT = BT / WGT / 32;   // 32x32 tiles per wave
-    constexpr int LR = 16 * NW;                 // stage rows one direct load fills
+    constexpr int LR = 8 * NW;                  // stage rows one direct load fills
     constexpr int LA = BJ / LR, LB = BT / LR;   // direct loads per thread per stage
-    static_assert(MJ >= 1 && MT >= 1 && LA * LR == BJ && LB * LR == BT, "tile shape");
-    constexpr int LPS = LA + LB;
     constexpr int STAGE_A = BJ * ROWB, STAGE = (BJ + BT) * ROWB;
     constexpr int NFR = MJ + MT, NMF = MJ * MT;
+    static_assert(MJ >= 1 && MT >= 1 && LA * LR == BJ && LB * LR == BT, "tile shape");
+    static_assert(WGT % 2 == 0, "token halves belong to whole rows of waves");
+    static_assert(NS >= 2 && NS <= 4, "two to four stages");
     // One __shared__ array per stage, always indexed by a compile-time stage
-    // number: the compiler can then tell which array a direct load writes and
-    // waits only for the loads of the stage it is about to read.
+    // number, so the compiler can tell which array a direct load writes.
     __shared__ __attribute__((aligned(1024))) char st0[STAGE];
     __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-    __shared__ __attribute__((aligned(1024))) char st2[STAGE];
-    __shared__ __attribute__((aligned(1024))) char st3[STAGE];
-    static_assert(NS == 4, "four stage arrays");
-    static_assert(STAGE >= (BT / 4) * BJ * 2, "a quarter of the out tile must fit a stage");
+    __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? STAGE : 16];
     auto stage = [&](auto S) __attribute__((always_inline)) -> char * {
         if constexpr (decltype(S)::value == 0) return st0;
         else if constexpr (decltype(S)::value == 1) return st1;
@@ -119,75 +124,72 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wj = w / WGT, wt = w % WGT;
     const int nchunk = L >> 3;
-    // K steps, padded to whole trips of NS steps; padded steps read zeros
-    // (KTAIL masking), so every trip has the same straight-line body.
-    const int nk = ((L + BK * NS - 1) / (BK * NS)) * NS;
+    // K stages, padded to a multiple of NS (padded chunks read zeros), so the
+    // array of every step is known at compile time.
+    const int nk = ((L + NS * BK - 1) / (NS * BK)) * NS;
     const uint32_t row_bytes = (uint32_t)L * 2u;
 
     // ---- buffer resources clipped to this tile's rows: overhanging rows read 0
     const int rows_a = min(BJ, n - j0);
     const int rows_b = (int)min((int64_t)BT, T - t0);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Wn + (int64_t)j0 * L), (short)0, (int)((uint32_t)rows_a * row_bytes), RSRC_W3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Y + t0 * L), (short)0, (int)((uint32_t)rows_b * row_bytes), RSRC_W3);
+    const __amdgpu_buffer_rsrc_t ra = lt_rsrc(Wn + (int64_t)j0 * L, (uint32_t)rows_a * row_bytes);
+    const __amdgpu_buffer_rsrc_t rb = lt_rsrc(Y + t0 * L, (uint32_t)rows_b * row_bytes);
 
-    // ---- direct loads: lane i of wave w, load q -> stage row LR*q + 16w + i/4,
-    // LDS slot i%4, global chunk (slot ^ key(row)).
-    const int lrow = 16 * w + (l >> 2);
-    const int lslot = l & 3;
+    // ---- direct loads: lane i of wave w, load q -> stage row LR*q + 8w + i/8,
+    // LDS slot i%8, global chunk (slot ^ swz8(row)).
+    const int lrow = 8 * w + (l >> 3);
+    const int lslot = l & 7;
     uint32_t offa[LA], offb[LB];
     int cha[LA], chb[LB];
 #pragma unroll
     for (int q = 0; q < LA; ++q) {
         const int row = LR * q + lrow;
-        cha[q] = lslot ^ swz(row);
+        cha[q] = lslot ^ swz8(row);
         offa[q] = (uint32_t)row * row_bytes + (uint32_t)cha[q] * 16u;
     }
 #pragma unroll
     for (int q = 0; q < LB; ++q) {
         const int row = LR * q + lrow;
-        chb[q] = lslot ^ swz(row);
+        chb[q] = lslot ^ swz8(row);
         offb[q] = (uint32_t)row * row_bytes + (uint32_t)chb[q] * 16u;
     }
-    auto issue = [&](auto S, int s) __attribute__((always_inline)) {   // stage s goes to array S = s % NS
+    auto issue = [&](auto S, int s) __attribute__((always_inline)) {   // K stage s -> array S
         char *sa = stage(S);
         char *sb = sa + STAGE_A;
         const uint32_t kbyte = (uint32_t)s * ROWB;
 #pragma unroll
         for (int q = 0; q < LA; ++q) {
             uint32_t vo = offa[q] + kbyte;
-            if (KTAIL && s * 4 + cha[q] >= nchunk) vo = OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (LR * q + 16 * w) * ROWB),
+            if (KTAIL && s * CPR + cha[q] >= nchunk) vo = OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + (LR * q + 8 * w) * ROWB),
                                                      16, vo, 0, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < LB; ++q) {
             uint32_t vo = offb[q] + kbyte;
-            if (KTAIL && s * 4 + chb[q] >= nchunk) vo = OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + (LR * q + 16 * w) * ROWB),
+            if (KTAIL && s * CPR + chb[q] >= nchunk) vo = OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + (LR * q + 8 * w) * ROWB),
                                                      16, vo, 0, 0, 0);
         }
     };
 
-    // ---- fragment reads (byte offsets within a stage)
+    // ---- fragment reads: lane l reads row perm32(l % 32) of each 32-row
+    // block, chunk 2*ks + l/32 of the stage row for K slice ks.
     const int hsel = l >> 5;
     const int arow = wj * (BJ / WGJ) + perm32(l & 31);
     const int brow = wt * (BT / WGT) + perm32(l & 31);   // token of this lane's D column
-    int afr[2], bfr[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        afr[ks] = arow * ROWB + (((2 * ks + hsel) ^ swz(arow)) << 4);
-        bfr[ks] = STAGE_A + brow * ROWB + (((2 * ks + hsel) ^ swz(brow)) << 4);
-    }
-    auto read_frags = [&](auto S, int ks, bf16x8_t (&fa)[MJ], bf16x8_t (&fb)[MT]) {
+    const int abase = arow * ROWB, bbase = STAGE_A + brow * ROWB;
+    const int akey = swz8(arow), bkey = swz8(brow);      // perm32 keeps r % 32 -> same key per block
+    auto read_frags = [&](auto S, int ks, bf16x8_t (&fa)[MJ], bf16x8_t (&fb)[MT])
+        __attribute__((always_inline)) {
         const char *base = stage(S);
+        const int ca = ((2 * ks + hsel) ^ akey) << 4, cb = ((2 * ks + hsel) ^ bkey) << 4;
 #pragma unroll
         for (int mj = 0; mj < MJ; ++mj)
-            fa[mj] = *reinterpret_cast<const bf16x8_t *>(base + afr[ks] + mj * 32 * ROWB);
+            fa[mj] = *reinterpret_cast<const bf16x8_t *>(base + abase + mj * 32 * ROWB + ca);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            fb[mt] = *reinterpret_cast<const bf16x8_t *>(base + bfr[ks] + mt * 32 * ROWB);
+            fb[mt] = *reinterpret_cast<const bf16x8_t *>(base + bbase + mt * 32 * ROWB + cb);
     };
 
     f32x16_t acc[MJ][MT];
@@ -195,183 +197,221 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
     for (int mj = 0; mj < MJ; ++mj)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mj][mt] = f32x16_t{};
-    auto mfma_all = [&](const bf16x8_t (&fa)[MJ], const bf16x8_t (&fb)[MT]) {
+    // MFMAs [lo, hi) of the MJ x MT grid for one K slice
+    auto mfma_range = [&](const bf16x8_t (&fa)[MJ], const bf16x8_t (&fb)[MT], int lo, int hi)
+        __attribute__((always_inline)) {
 #pragma unroll
-        for (int mj = 0; mj < MJ; ++mj)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < NMF; ++i) {
+            if (i >= lo && i < hi) {
+                const int mj = i / MT, mt = i % MT;
                 acc[mj][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mj], fb[mt], acc[mj][mt],
                                                                       0, 0, 0);
+            }
+        }
     };
 
-    // ---- the out tile goes through LDS.  Quarter q (tile rows q*BT/4 ..,
-    // row-major, 16-byte chunks XOR-swizzled by row) arrives by direct loads in
-    // the stage array that tail step q has just freed, so its HBM latency
-    // overlaps the last MFMAs; the sums are then formed in place and the tile
-    // is written back row by row.
+    // ---- the out tile moves through LDS in two halves of BT/2 token rows
+    // (row-major, 16-byte chunks XOR-swizzled by row).
     constexpr int CPRE = BJ / 8;               // 16-byte chunks per tile row
-    constexpr int RPQ = BT / 4;                // tile rows per quarter
-    constexpr int QCH = RPQ * CPRE;            // chunks per quarter
-    constexpr int QLD = QCH / NT;              // direct loads per thread per quarter
-    static_assert(!EPI_LDS || QCH % NT == 0, "a quarter is whole workgroup loads");
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(outn + t0 * ld_out), (short)0,
-        (int)(((int64_t)max(rows_b - 1, 0) * ld_out + n) * 2), RSRC_W3);
-    auto load_c_quarter = [&](char *dst, int q) __attribute__((always_inline)) {
+    constexpr int RPH = BT / 2;                // tile rows per half
+    constexpr int HCH = RPH * CPRE;            // chunks per half
+    constexpr int HLD = HCH / NT;              // direct loads per thread per half
+    static_assert(!EPI_LDS || HCH % NT == 0, "a half is whole workgroup loads");
+    static_assert(RPH * BJ * 2 <= STAGE, "half of the out tile must fit a stage");
+    const __amdgpu_buffer_rsrc_t rc = lt_rsrc(
+        outn + t0 * ld_out, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_out + n) * 2));
+    auto load_c_half = [&](char *dst, int h) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < QLD; ++it) {
+        for (int it = 0; it < HLD; ++it) {
             const int idx0 = it * NT + 64 * w;      // wave-uniform
             const int idx = idx0 + l;
-            const int r = q * RPQ + idx / CPRE;
+            const int r = h * RPH + idx / CPRE;
             const int c = (idx % CPRE) ^ (r & (CPRE - 1));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rc, (lds_void *)(dst + idx0 * 16), 16,
                 (uint32_t)(((int64_t)r * ld_out + j0 + 8 * c) * 2), 0, 0, 0);
         }
     };
-    auto stage_dyn = [&](int i) __attribute__((always_inline)) -> char * {
-        return i == 0 ? st0 : i == 1 ? st1 : i == 2 ? st2 : st3;
-    };
 
-    // One K step on stage array S (= kb % NS): MFMA half 0 (fragments already
-    // in f0), barrier for the next stage between the halves, MFMA half 1.  The
-    // array freed by the previous step (SP) receives stage kb+NS-1 (CQ < 0),
-    // quarter CQ of the out tile (0 <= CQ < 4), or nothing.  WAIT is the
-    // number of vector loads allowed to stay in flight at the barrier; the
-    // last step (LAST) has no barrier.
-    bf16x8_t f0a[MJ], f0b[MT], f1a[MJ], f1b[MT];
-    auto step = [&](auto S, auto CQ, auto WAIT, auto LAST, int kb) __attribute__((always_inline)) {
-        constexpr int s = decltype(S)::value;
-        constexpr int cq = decltype(CQ)::value;
-        using SN = std::integral_constant<int, (s + 1) % NS>;
-        using SP = std::integral_constant<int, (s + NS - 1) % NS>;
-        if constexpr (cq < 0) issue(SP{}, kb + NS - 1);
-        else if constexpr (cq < 4) load_c_quarter(stage(SP{}), cq);
-        read_frags(S, 1, f1a, f1b);
-        mfma_all(f0a, f0b);
+    // One K stage on array S.  On entry fa/fb[0] hold slice 0's fragments.
+    // First the array freed by the previous stage, (S + NS - 1) % NS, receives
+    // K stage kb + NS - 1 (ACT < 0), half ACT of the out tile (0, 1), or
+    // nothing (2).  Slices alternate between the two fragment buffers; the
+    // barrier sits inside the last slice, after waiting until at most WAIT
+    // loads of this thread are in flight (the next stage has landed), and is
+    // followed by the next stage's slice-0 reads.  The last stage has none.
+    bf16x8_t fa[2][MJ], fb[2][MT];
+    // scheduling hint: alternate the ND fragment reads with the NM MFMAs
+    // just emitted, then the rest of whichever is longer
+    auto interleave = [&](auto ND, auto NM) __attribute__((always_inline)) {
+        constexpr int nd = decltype(ND)::value, nm = decltype(NM)::value;
+        constexpr int np = nd < nm ? nd : nm;
 #pragma unroll
-        for (int i = 0; i < NFR; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int i = 0; i < np; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NFR, 0);
-        if constexpr (!decltype(LAST)::value) {
+        if constexpr (nm > np) __builtin_amdgcn_sched_group_barrier(0x008, nm - np, 0);
+        if constexpr (nd > np) __builtin_amdgcn_sched_group_barrier(0x100, nd - np, 0);
+    };
+    auto kstage = [&](auto S, auto ACT, auto WAIT, auto LAST, int kb) __attribute__((always_inline)) {
+        constexpr int s = decltype(S)::value;
+        constexpr int act = decltype(ACT)::value;
+        constexpr bool last = decltype(LAST)::value;
+        using SN = I<(s + 1) % NS>;
+        using SP = I<(s + NS - 1) % NS>;
+        if constexpr (act < 0) issue(SP{}, kb + NS - 1);
+        else if constexpr (act < 2 && EPI_LDS) load_c_half(stage(SP{}), act);
+        // keep the loads at the top of the stage: left to itself the scheduler
+        // sinks them next to the wait at the barrier, serialising them with
+        // the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KSL - 1; ++ks) {
+            read_frags(S, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            mfma_range(fa[ks & 1], fb[ks & 1], 0, NMF);
+            interleave(I<NFR>{}, I<NMF>{});
+        }
+        constexpr int KL = (KSL - 1) & 1;
+        constexpr int HALF = NMF / 2;
+        mfma_range(fa[KL], fb[KL], 0, HALF);
+        if constexpr (!last) {
             __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(decltype(WAIT)::value));
             lt_lds_barrier();
-            read_frags(SN{}, 0, f0a, f0b);
+            read_frags(SN{}, 0, fa[0], fb[0]);
         }
-        mfma_all(f1a, f1b);
-        // interleave: half-1 fragment reads between half-0 MFMAs (above), the
-        // next stage's first reads between half-1 MFMAs (below)
-#pragma unroll
-        for (int i = 0; i < NFR; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NFR, 0);
+        mfma_range(fa[KL], fb[KL], HALF, NMF);
+        if constexpr (!last) interleave(I<NFR>{}, I<NMF - HALF>{});
     };
-    // ---- prologue: stages 0 .. NS-2 in flight, wait for stage 0
+    using F = std::false_type;
+    using Tr = std::true_type;
+    constexpr int LPS = LA + LB;                 // stage loads per thread
+    constexpr int HQ = EPI_LDS ? HLD : 0;        // out-half loads per thread
+
+    // ---- prologue: K stages 0 .. NS-2 in flight, wait for stage 0
     issue(I<0>{}, 0);
-    issue(I<1>{}, 1);
-    issue(I<2>{}, 2);
+    if constexpr (NS > 2) issue(I<1>{}, 1);
+    if constexpr (NS > 3) issue(I<2>{}, 2);
     __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0((NS - 2) * LPS));
     lt_lds_barrier();
-    read_frags(I<0>{}, 0, f0a, f0b);
+    read_frags(I<0>{}, 0, fa[0], fb[0]);
 
-    // ---- K loop: NS steps per trip (one per stage array), each issuing stage
-    // kb+NS-1 and leaving NS-2 stages in flight.  The last trip is peeled: its
-    // first step issues the last stage, the other three issue no stage but
-    // load out-tile quarters 0..2 into the arrays just freed (arrays 0..2).
-    constexpr int W_MAIN = (NS - 2) * LPS;
+    constexpr int WM = (NS - 2) * LPS;           // steady state: NS-2 stages stay in flight
     for (int kb = 0; kb < nk - NS; kb += NS) {
-        step(I<0>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb);
-        step(I<1>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb + 1);
-        step(I<2>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb + 2);
-        step(I<3>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb + 3);
+        kstage(I<0>{}, I<-1>{}, I<WM>{}, F{}, kb);
+        kstage(I<1>{}, I<-1>{}, I<WM>{}, F{}, kb + 1);
+        if constexpr (NS > 2) kstage(I<2>{}, I<-1>{}, I<WM>{}, F{}, kb + 2);
+        if constexpr (NS > 3) kstage(I<3>{}, I<-1>{}, I<WM>{}, F{}, kb + 3);
     }
+    // last trip: the first step issues the last K stage; with three or more
+    // stages the next two steps fetch the out-tile halves into arrays 0 and 1,
+    // with two the last step fetches half 0 into array 0
     {
         const int kb = nk - NS;
-        constexpr int C0 = EPI_LDS ? 0 : 4, C1 = EPI_LDS ? 1 : 4, C2 = EPI_LDS ? 2 : 4;
-        constexpr int Q = EPI_LDS ? QLD : 0;
-        step(I<0>{}, I<-1>{}, I<W_MAIN>{}, B<false>{}, kb);
-        step(I<1>{}, I<C0>{}, I<LPS + Q>{}, B<false>{}, kb + 1);
-        step(I<2>{}, I<C1>{}, I<2 * Q>{}, B<false>{}, kb + 2);
-        step(I<3>{}, I<C2>{}, I<0>{}, B<true>{}, kb + 3);
+        if constexpr (NS == 2) {
+            kstage(I<0>{}, I<-1>{}, I<0>{}, F{}, kb);
+            kstage(I<1>{}, I<0>{}, I<0>{}, Tr{}, kb + 1);
+        } else if constexpr (NS == 3) {
+            kstage(I<0>{}, I<-1>{}, I<LPS>{}, F{}, kb);
+            kstage(I<1>{}, I<0>{}, I<HQ>{}, F{}, kb + 1);
+            kstage(I<2>{}, I<1>{}, I<0>{}, Tr{}, kb + 2);
+        } else {
+            kstage(I<0>{}, I<-1>{}, I<2 * LPS>{}, F{}, kb);
+            kstage(I<1>{}, I<0>{}, I<LPS + HQ>{}, F{}, kb + 1);
+            kstage(I<2>{}, I<1>{}, I<2 * HQ>{}, F{}, kb + 2);
+            kstage(I<3>{}, I<2>{}, I<0>{}, Tr{}, kb + 3);
+        }
     }
 
     if constexpr (EPI_LDS) {
-        // quarter 3 goes into array 3 once every wave is done with it
-        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));   // LDS reads done
-        lt_lds_barrier();
-        load_c_quarter(st3, 3);
-        __builtin_amdgcn_s_waitcnt(0);
-        lt_lds_barrier();
-        auto stage_row = [&](int r) __attribute__((always_inline)) -> char * {
-            return stage_dyn(r / RPQ) + (r % RPQ) * (BJ * 2);
-        };
-        // ---- sums in place: out + acc, one rounding
+        // half 0 goes to st0 and half 1 to st1.  With two stages half 1 is
+        // fetched here, once every wave is past its last reads of st1; with
+        // more it is already in flight.
+        if constexpr (NS == 2) {
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+            lt_lds_barrier();
+            load_c_half(st1, 1);
+        } else {
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(HLD));
+            lt_lds_barrier();
+        }
+        // sums in place for the rows this wave owns (its token half h = wt / (WGT/2))
+        const int h = wt / (WGT / 2);
+        auto sums = [&](char *half) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int r = brow + 32 * mt;
+            for (int mt = 0; mt < MT; ++mt) {
+                const int r = brow + 32 * mt;             // tile row (token)
+                const int rh = r - h * RPH;               // row within the half
 #pragma unroll
-            for (int mj = 0; mj < MJ; ++mj) {
+                for (int mj = 0; mj < MJ; ++mj) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int c = (wj * (BJ / WGJ) + 32 * mj + 16 * half + 8 * hsel) >> 3;
-                    const f32x16_t &a = acc[mj][mt];
-                    u32x4_t *ptr = reinterpret_cast<u32x4_t *>(stage_row(r) +
-                                                               ((c ^ (r & (CPRE - 1))) << 4));
-                    u32x4_t ov = *ptr;
-                    // The buffer range check is per dword: a chunk that straddles
-                    // the window end can come back with its last valid column
-                    // zeroed.  Re-read that chunk's valid columns directly.
-                    const int jc = j0 + 8 * c;
-                    if (jc < n && jc + 8 > n && t0 + r < T) {
-                        const u16 *src = outn + (t0 + r) * ld_out + jc;
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int c = (wj * (BJ / WGJ) + 32 * mj + 16 * hf + 8 * hsel) >> 3;
+                        const f32x16_t &a = acc[mj][mt];
+                        u32x4_t *ptr = reinterpret_cast<u32x4_t *>(
+                            half + rh * (BJ * 2) + ((c ^ (r & (CPRE - 1))) << 4));
+                        u32x4_t ov = *ptr;
+                        // The buffer range check is per dword: a chunk that
+                        // straddles the window end can come back with its last
+                        // valid column zeroed.  Re-read its valid columns.
+                        const int jc = j0 + 8 * c;
+                        if (jc < n && jc + 8 > n && t0 + r < T) {
+                            const u16 *src = outn + (t0 + r) * ld_out + jc;
 #pragma unroll
-                        for (int e = 0; e < 8; e += 2) {
-                            const uint32_t lo = (jc + e < n) ? src[e] : 0u;
-                            const uint32_t hi = (jc + e + 1 < n) ? src[e + 1] : 0u;
-                            ov[e >> 1] = lo | (hi << 16);
+                            for (int e = 0; e < 8; e += 2) {
+                                const uint32_t lo = (jc + e < n) ? src[e] : 0u;
+                                const uint32_t hi = (jc + e + 1 < n) ? src[e + 1] : 0u;
+                                ov[e >> 1] = lo | (hi << 16);
+                            }
                         }
+                        u32x4_t nv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            nv[e] = lt_pack2(lt_bf_lo(ov[e]) + a[8 * hf + 2 * e],
+                                             lt_bf_hi(ov[e]) + a[8 * hf + 2 * e + 1]);
+                        *ptr = nv;
                     }
-                    u32x4_t nv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        nv[e] = lt_pack2(lt_bf_lo(ov[e]) + a[8 * half + 2 * e],
-                                         lt_bf_hi(ov[e]) + a[8 * half + 2 * e + 1]);
-                    *ptr = nv;
                 }
             }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        lt_lds_barrier();
-        // ---- write back whole row segments
-        constexpr int LPR = CPRE;                     // lanes per tile row
-        constexpr int RPI = 64 / LPR;                 // rows per store instruction
-        constexpr int ROWS_W = BT / NW;               // rows per wave
-        static_assert(ROWS_W % RPI == 0, "whole store rounds per wave");
+        };
+        // write back rows [r_lo, r_lo + nrows) of half hh, spread over nwv waves (wave index wi)
+        constexpr int LPR = CPRE;                    // lanes per tile row
+        constexpr int RPI = 64 / LPR;                // rows per store instruction
         static_assert(CPRE <= 64, "row wider than a wave");
-#pragma unroll 4
-        for (int i = 0; i < ROWS_W / RPI; ++i) {
-            const int r = w * ROWS_W + i * RPI + l / LPR;
-            const int c = l % LPR;
-            const int64_t t = t0 + r;
-            const int j = j0 + 8 * c;
-            if (t < T && j < n) {
-                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
-                    stage_row(r) + ((c ^ (r & (CPRE - 1))) << 4));
-                if (j + 8 <= n) {
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        v, rc, (uint32_t)(((int64_t)r * ld_out + j) * 2), 0, 0);
-                } else {
-                    u16 *o = outn + t * ld_out + j;
+        auto write_back = [&](const char *half, int hh, int wi, int nwv) __attribute__((always_inline)) {
+            const int per = RPH / nwv;
+            for (int i = 0; i < per / RPI; ++i) {
+                const int rh = wi * per + i * RPI + l / LPR;
+                const int r = hh * RPH + rh;
+                const int c = l % LPR;
+                const int64_t t = t0 + r;
+                const int j = j0 + 8 * c;
+                if (t < T && j < n) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+                        half + rh * (BJ * 2) + ((c ^ (r & (CPRE - 1))) << 4));
+                    if (j + 8 <= n) {
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v, rc, (uint32_t)(((int64_t)r * ld_out + j) * 2), 0, 0);
+                    } else {
+                        u16 *o = outn + t * ld_out + j;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (j + e < n) o[e] = (u16)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                        for (int e = 0; e < 8; ++e)
+                            if (j + e < n) o[e] = (u16)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                    }
                 }
             }
-        }
+        };
+        static_assert((RPH / (NW / 2)) % RPI == 0 && (RPH / NW) % RPI == 0, "whole store rounds");
+        if (h == 0) sums(st0);
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+        lt_lds_barrier();
+        // half 1 has landed and half 0 is summed: the half-1 waves sum while
+        // the half-0 waves write half 0 back
+        if (h == 1) sums(st1);
+        else write_back(st0, 0, wj * (WGT / 2) + wt, NW / 2);
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+        lt_lds_barrier();
+        write_back(st1, 1, w, NW);
     } else {
         // ---- plain epilogue (unaligned `out`): element-wise read-add-round-write
 #pragma unroll
@@ -382,13 +422,13 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
 #pragma unroll
             for (int mj = 0; mj < MJ; ++mj) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int j = j0 + wj * (BJ / WGJ) + 32 * mj + 16 * half + 8 * hsel;
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int j = j0 + wj * (BJ / WGJ) + 32 * mj + 16 * hf + 8 * hsel;
                     const f32x16_t &a = acc[mj][mt];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         if (j + e < n) {
-                            const float v = lt_bf_lo((uint32_t)orow[j + e]) + a[8 * half + e];
+                            const float v = lt_bf_lo((uint32_t)orow[j + e]) + a[8 * hf + e];
                             orow[j + e] = (u16)(lt_pack2(v, 0.f) & 0xFFFFu);
                         }
                     }
@@ -398,7 +438,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
     }
 }
 
-template <int BJ, int BT, int WGJ, int WGT, int GROUP_J>
+template <int BJ, int BT, int WGJ, int WGT, int NS, int GROUP_J>
 hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 *outn,
                       int64_t ld_out, bool vec16, hipStream_t stream)
 {
@@ -406,16 +446,16 @@ hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 
     const int64_t ntt = (T + BT - 1) / BT;
     if ((int64_t)ntj * ntt > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(ntj * ntt)), block(64 * WGJ * WGT);
-    // The LDS epilogue moves whole out-tile quarters with workgroup-wide 16-byte
+    // The LDS epilogue moves whole out-tile halves with workgroup-wide 16-byte
     // direct loads and addresses `out` through 32-bit buffer offsets: it needs
-    // an aligned window and a tile extent below 2 GiB; anything else (and tiles
-    // too small for whole-workgroup quarters) takes the plain epilogue.
-    constexpr bool EPI_OK = ((BT / 4) * (BJ / 8)) % (64 * WGJ * WGT) == 0;
+    // an aligned window and a tile extent below 2 GiB; anything else takes the
+    // plain epilogue.
+    constexpr bool EPI_OK = ((BT / 2) * (BJ / 8)) % (64 * WGJ * WGT) == 0;
     const bool epi = EPI_OK && vec16 && (int64_t)BT * ld_out * 2 < ((int64_t)1 << 31);
 #define LT_GEMM_LAUNCH(KT, EPI)                                                              \
-    hipLaunchKernelGGL((k_gemm<BJ, BT, WGJ, WGT, GROUP_J, KT, EPI>), grid, block, 0, stream, y, T, L, Wn, \
-                       n, outn, ld_out, ntj, (int)ntt)
-    const bool kt = L % (BK * NS) != 0;
+    hipLaunchKernelGGL((k_gemm<BJ, BT, WGJ, WGT, NS, GROUP_J, KT, EPI>), grid, block, 0, stream, y, T, \
+                       L, Wn, n, outn, ld_out, ntj, (int)ntt)
+    const bool kt = L % (NS * BK) != 0;
     if constexpr (EPI_OK) {
         if (epi) {
             if (kt) LT_GEMM_LAUNCH(true, true); else LT_GEMM_LAUNCH(false, true);
@@ -433,18 +473,19 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
                        uint16_t *outn, int64_t ld_out, hipStream_t stream)
 {
     const bool vec16 = ((reinterpret_cast<uintptr_t>(outn) & 15) == 0) && (ld_out % 8 == 0);
-    // Tile shape by tile count (measured on n = 7168, T = 128 .. 8192): the
-    // largest tile that still gives about one tile per CU.  The big tiles run
-    // 8 waves (two per SIMD, which hide each other's LDS and barrier waits);
-    // the 64 x 128 tile runs 4 waves and three workgroups per CU.
+    // Tile shape and stage count by tile count (measured on n = 7168, T = 128
+    // .. 8192, random data): the biggest tile that still gives about one tile
+    // per CU.  256 x 256 and 128 x 128 tiles run 8 waves (two per SIMD, which
+    // hide each other's LDS and barrier waits); below a full round of tiles,
+    // four stages in flight hide the L2 latency that two stages leave exposed.
     auto tiles = [&](int bj, int bt) { return (int64_t)((n + bj - 1) / bj) * ((T + bt - 1) / bt); };
     if (tiles(256, 256) >= 224)
-        return launch_cfg<256, 256, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
-    if (tiles(128, 256) >= 224)
-        return launch_cfg<128, 256, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+        return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+    if (tiles(128, 128) >= 448)
+        return launch_cfg<128, 128, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
     if (tiles(128, 128) >= 224)
-        return launch_cfg<128, 128, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
-    return launch_cfg<64, 128, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+        return launch_cfg<128, 128, 4, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+    return launch_cfg<64, 128, 2, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
 }
 
 }  // namespace lt

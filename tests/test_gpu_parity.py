@@ -109,10 +109,10 @@ def test_large_workload_sampled(name):
 
 
 @pytest.mark.parametrize("T,n,c0,ld,P", [
-    (2000, 7100, 37, 7168, 2),   # 256 x 256 tiles, 8 waves (224 tiles), ragged both ways
-    (1000, 7100, 5, 7120, 1),    # 128 x 256 tiles, 8 waves
-    (500, 7100, 11, 7128, 3),    # 128 x 128 tiles, 8 waves
-    (300, 3000, 8, 3016, 1),     # 64 x 128 tiles, 4 waves
+    (2000, 7100, 37, 7168, 2),   # 256 x 256 tiles, 2 stages (224 tiles), ragged both ways
+    (1000, 7100, 5, 7120, 1),    # 128 x 128 tiles, 2 stages
+    (500, 7100, 11, 7128, 3),    # 128 x 128 tiles, 4 stages
+    (300, 3000, 8, 3016, 1),     # 64 x 128 tiles, 4 waves, 4 stages
 ])
 def test_gemm_tile_shapes_sampled(T, n, c0, ld, P):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
