@@ -337,6 +337,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
         }
         // sums in place for the rows this wave owns (its token half h = wt / (WGT/2))
         const int h = wt / (WGT / 2);
+        const bool edge = j0 + BJ > n;            // the window ends inside this tile
         auto sums = [&](char *half) __attribute__((always_inline)) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
                         // straddles the window end can come back with its last
                         // valid column zeroed.  Re-read its valid columns.
                         const int jc = j0 + 8 * c;
-                        if (jc < n && jc + 8 > n && t0 + r < T) {
+                        if (edge && jc < n && jc + 8 > n && t0 + r < T) {
                             const u16 *src = outn + (t0 + r) * ld_out + jc;
 #pragma unroll
                             for (int e = 0; e < 8; e += 2) {

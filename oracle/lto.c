@@ -195,3 +195,41 @@ int lto_latent_tail(const uint16_t *partials, int P, int64_t T, int64_t L,
     free(y);
     return 0;
 }
+
+/*
+ * The tail followed by the decoder layer's residual update, on the window.
+ *
+ * [PR50593 Key source snippets, `forward_attn_residual`]: after the MLP the
+ * layer adds the MLP output to the running prefix sum, `prefix_sum +
+ * hidden_states`, as a bf16 add (one rounding of the exact sum).  Here the
+ * MLP output is the tail's result, so after lto_latent_tail
+ *
+ *   resid[t, c0+j] = bf16( prefix[t, c0+j] + out[t, c0+j] )       (R4)
+ *
+ * for t < T, 0 <= j < n, with out already updated by R3.  Columns outside the
+ * window of resid are left untouched.  resid may be the prefix buffer itself
+ * (same pointer and row stride): every element is read before it is written.
+ *
+ * prefix: [T][ld_prefix], resid: [T][ld_resid] bf16 bits, ld >= c0 + n.
+ * Returns 0, or -1 on bad arguments.
+ */
+int lto_latent_tail_residual(const uint16_t *partials, int P, int64_t T, int64_t L,
+                             const uint16_t *norm_w, double eps,
+                             const uint16_t *W, int64_t H, int64_t c0, int64_t n,
+                             uint16_t *out, int64_t ld_out,
+                             const uint16_t *prefix, int64_t ld_prefix,
+                             uint16_t *resid, int64_t ld_resid, int nthreads)
+{
+    if (ld_prefix < c0 + n || ld_resid < c0 + n) return -1;
+    if (T > 0 && n > 0 && (!prefix || !resid)) return -1;
+    int rc = lto_latent_tail(partials, P, T, L, norm_w, eps, W, H, c0, n, out, ld_out, nthreads);
+    if (rc != 0) return rc;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = c0; j < c0 + n; ++j) {
+            const double a = lto_bf16_to_f64(prefix[t * ld_prefix + j]);
+            const double b = lto_bf16_to_f64(out[t * ld_out + j]);
+            resid[t * ld_resid + j] = lto_f64_to_bf16(a + b);
+        }
+    }
+    return 0;
+}

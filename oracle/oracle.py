@@ -55,6 +55,10 @@ def _load():
     lib.lto_latent_tail.argtypes = [u16p, ctypes.c_int, i64, i64, u16p, ctypes.c_double,
                                     u16p, i64, i64, i64, u16p, i64, ctypes.c_int]
     lib.lto_latent_tail.restype = ctypes.c_int
+    lib.lto_latent_tail_residual.argtypes = [u16p, ctypes.c_int, i64, i64, u16p, ctypes.c_double,
+                                             u16p, i64, i64, i64, u16p, i64, u16p, i64, u16p,
+                                             i64, ctypes.c_int]
+    lib.lto_latent_tail_residual.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -125,3 +129,35 @@ def latent_tail(partials, norm_w, eps, W, c0, n, out, nthreads=0):
     if rc != 0:
         raise ValueError("lto_latent_tail rejected its arguments")
     return o
+
+
+def latent_tail_residual(partials, norm_w, eps, W, c0, n, out, prefix, resid=None,
+                         in_place=False, nthreads=0):
+    """Return (out', resid') copies: the tail's updated ``out`` and the
+    residual buffer with bf16(prefix + out') written on the window.
+
+    prefix [T][ld_prefix]; resid [T][ld_resid] (its columns outside the window
+    are kept) or None for a copy of prefix; in_place=True passes the prefix
+    buffer itself as resid (resid must then be None).
+    """
+    p = _u16(partials)
+    P, T, L = p.shape
+    Wm = _u16(W)
+    H = Wm.shape[0]
+    w = _u16(norm_w)
+    o = np.array(_u16(out), copy=True)
+    pre = np.array(_u16(prefix), copy=True)
+    if in_place:
+        if resid is not None:
+            raise ValueError("in_place takes no separate resid")
+        r = pre
+    else:
+        r = np.array(_u16(resid if resid is not None else prefix), copy=True)
+    if o.ndim != 2 or o.shape[0] != T or pre.shape[0] != T or r.shape[0] != T:
+        raise ValueError("out, prefix and resid must have T rows")
+    rc = _load().lto_latent_tail_residual(_ptr(p), P, T, L, _ptr(w), float(eps), _ptr(Wm), H,
+                                          int(c0), int(n), _ptr(o), o.shape[1], _ptr(pre),
+                                          pre.shape[1], _ptr(r), r.shape[1], int(nthreads))
+    if rc != 0:
+        raise ValueError("lto_latent_tail_residual rejected its arguments")
+    return o, r

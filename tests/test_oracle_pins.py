@@ -131,6 +131,27 @@ def test_hand_worked_example(oracle_mod):
     np.testing.assert_array_equal(got0, bits_of(g["expected_out_nonorm"]).reshape(T, ld))
 
 
+def test_hand_worked_residual(oracle_mod):
+    """The residual update of the hand example, including a tie that rounds
+    to the even neighbour, with and without the norm, separate and in place."""
+    g = _read_golden("hand_example.txt")
+    T, L, H, P = (int(g[k][0]) for k in ("T", "L", "H", "P"))
+    ld, c0, n = (int(g[k][0]) for k in ("ld_out", "c0", "n"))
+    eps = g["eps"][0]
+    partials = bits_of(g["partials"]).reshape(P, T, L)
+    norm_w = bits_of(g["norm_w"])
+    W = bits_of(g["W"]).reshape(H, L)
+    out = bits_of(g["out"]).reshape(T, ld)
+    prefix = bits_of(g["prefix"]).reshape(T, ld)
+    for nw, ko, kr in ((norm_w, "expected_out", "expected_resid"),
+                       (None, "expected_out_nonorm", "expected_resid_nonorm")):
+        for in_place in (False, True):
+            o, r = oracle_mod.latent_tail_residual(partials, nw, eps, W, c0, n, out, prefix,
+                                                   in_place=in_place)
+            np.testing.assert_array_equal(o, bits_of(g[ko]).reshape(T, ld))
+            np.testing.assert_array_equal(r, bits_of(g[kr]).reshape(T, ld))
+
+
 # --------------------------------------------------------------------------
 # RMSNorm closed forms
 # --------------------------------------------------------------------------
@@ -387,3 +408,53 @@ def test_brute_force_three_partials_window(oracle_mod):
 def test_brute_force_norm_disabled(oracle_mod):
     wl = synth.Workload("bf0", T=2, L=48, H=16, P=2, c0=3, n=9, ld_out=16, norm=False)
     _brute_force_check(oracle_mod, wl, 17, EPS32)
+
+
+# --------------------------------------------------------------------------
+# residual update after the tail
+# --------------------------------------------------------------------------
+
+def test_residual_matches_torch_bf16_add(oracle_mod):
+    """R4 is PyTorch's bf16 add of the prefix and the tail's output (the sum
+    of two bf16 values rounds correctly through float32), checked against
+    torch on a ragged window, with prefix outliers and ties."""
+    import torch
+
+    wl = synth.Workload("res", T=7, L=72, H=40, P=2, c0=3, n=29, ld_out=45, part_std=0.6,
+                        outlier_density=0.05)
+    d = synth.generate(wl, seed=21)
+    rng = np.random.Generator(np.random.PCG64(5))
+    prefix = synth.to_bf16_bits(rng.standard_normal((wl.T, wl.ld_out + 2)) * 4.0)
+    resid0 = synth.to_bf16_bits(rng.standard_normal((wl.T, wl.ld_out + 2)))
+    out_new = oracle_mod.latent_tail(d["partials"], d["norm_w"], EPS32, d["W"], wl.c0, wl.n,
+                                     d["out"])
+    o, r = oracle_mod.latent_tail_residual(d["partials"], d["norm_w"], EPS32, d["W"], wl.c0,
+                                           wl.n, d["out"], prefix, resid=resid0)
+    np.testing.assert_array_equal(o, out_new)
+    win = slice(wl.c0, wl.c0 + wl.n)
+    tp = torch.from_numpy(prefix[:, win].astype(np.int16)).view(torch.bfloat16)
+    to = torch.from_numpy(out_new[:, win].astype(np.int16)).view(torch.bfloat16)
+    want = (tp + to).view(torch.int16).numpy().astype(np.uint16)
+    np.testing.assert_array_equal(r[:, win], want)
+    keep = np.ones(r.shape, dtype=bool)
+    keep[:, win] = False
+    np.testing.assert_array_equal(r[keep], resid0[keep])
+
+
+def test_residual_of_zero_prefix_is_the_output(oracle_mod):
+    """prefix = +0: the residual window equals the tail's output value for
+    value (bf16(0 + x) = x; a -0 output becomes +0)."""
+    wl = synth.Workload("res0", T=5, L=64, H=33, P=1, c0=0, n=33, ld_out=33)
+    d = synth.generate(wl, seed=4)
+    prefix = np.zeros((wl.T, wl.ld_out), dtype=np.uint16)
+    o, r = oracle_mod.latent_tail_residual(d["partials"], d["norm_w"], EPS32, d["W"], 0, wl.n,
+                                           d["out"], prefix)
+    np.testing.assert_array_equal(synth.bf16_bits_to_f64(r), synth.bf16_bits_to_f64(o))
+
+
+def test_residual_rejects_short_strides(oracle_mod):
+    wl = synth.Workload("resb", T=2, L=8, H=6, P=1, c0=2, n=4, ld_out=6)
+    d = synth.generate(wl, seed=1)
+    with pytest.raises(ValueError):
+        oracle_mod.latent_tail_residual(d["partials"], d["norm_w"], EPS32, d["W"], 2, 4,
+                                        d["out"], np.zeros((2, 5), dtype=np.uint16))
