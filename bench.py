@@ -127,6 +127,54 @@ def gemm_traffic_bytes():
     return None
 
 
+RES_T = [1, 16, 1024, 8192]
+
+
+def residual_pass(binding, hip, stream, sh, sets, wpool, norm_w, call_kern, reps=20):
+    """The residual form (the tail plus the decoder layer's prefix-sum update,
+    fused into the epilogue) against the unfused pair: the tail, then a
+    separate bf16 add of prefix + out (PyTorch's elementwise kernel on the
+    same stream).  Kernel times from HIP events around each launch."""
+    import numpy as np
+    import torch
+
+    res = {}
+    with torch.cuda.stream(stream):
+        for T in RES_T:
+            pre = [torch.randn(T, H, device="cuda").to(torch.bfloat16) for _ in range(2)]
+            rsd = [torch.empty_like(p) for p in pre]
+            ev = [(hip.event(), hip.event(), hip.event(), hip.event()) for _ in range(reps)]
+            for i in range(reps + 2):
+                p, o = sets[T][i % len(sets[T])]
+                W = wpool[(7 * i) % len(wpool)]
+                e = ev[i - 2] if i >= 2 else None
+                if e:
+                    binding.lt_set_kernel_events(e[0], e[1])
+                binding.check(binding.lt_latent_tail_residual(
+                    p, P, T, L, norm_w, EPS, W, H, 0, H, o, H, pre[i % 2], H, rsd[i % 2], H, sh))
+                binding.lt_set_kernel_events(None, None)
+                if e:
+                    hip.record(e[2], sh)
+                torch.add(pre[i % 2], o.view(torch.bfloat16), out=rsd[i % 2])
+                if e:
+                    hip.record(e[3], sh)
+            torch.cuda.synchronize()
+            fused = float(np.mean([hip.elapsed_ms(e[0], e[1]) * 1e3 for e in ev]))
+            add = float(np.mean([hip.elapsed_ms(e[2], e[3]) * 1e3 for e in ev]))
+            for e in ev:
+                for x in e:
+                    hip.destroy(x)
+            res[str(T)] = {
+                "fused_kernel_us": round(fused, 3),
+                "tail_kernel_us": round(call_kern[T], 3),
+                "separate_add_us": round(add, 3),
+                "unfused_us": round(call_kern[T] + add, 3),
+                "extra_bytes": 4 * T * H,
+            }
+            del pre, rsd
+    return res
+
+
 def cpu_baseline(d, target_s=12.0):
     """The fp64 oracle as it stands on this host's cores, on the first S tokens
     of the T=8192 call (S sized for ~target_s seconds of work)."""
@@ -300,6 +348,8 @@ def main():
             for e in e4:
                 hip.destroy(e)
 
+    residual = residual_pass(binding, hip, stream, sh, sets, wpool, norm_w, call_kern=kern_us)
+
     total_flops = K * sum(flops_of(T) for T in T_SWEEP)
     total_w = K * nT * 2 * H * L
     value = total_flops / wall / 1e12
@@ -359,6 +409,7 @@ def main():
         "per_T": per_T,
         "roofline": roofline,
         "roofline_skinny": roofline_skinny,
+        "residual": residual,
     }
     if not args.no_cpu:
         log("timing the CPU oracle ...")

@@ -101,6 +101,44 @@ LT_API int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64
                    const void *norm_w, float eps, const void *W, int64_t H,
                    int64_t c0, int64_t n, void *out, int64_t ld_out, void *stream);
 
+/*
+ * lt_latent_tail_residual -- lt_latent_tail followed by the decoder layer's
+ * residual update, fused into the tail's epilogue.
+ *
+ * [PR50593 Key source snippets, `forward_attn_residual`]: after the MLP the
+ * layer adds the MLP output to the running prefix sum (a bf16 add, one
+ * rounding of the exact sum).  With the tail's result as the MLP output:
+ * after updating `out` exactly as lt_latent_tail does, for t < T and
+ * 0 <= j < n
+ *
+ *   resid[t][c0+j] = bf16( prefix[t][c0+j] + out[t][c0+j] )
+ *
+ * using the updated (already rounded) out, so the result equals running the
+ * tail and then the separate add.  The add of the pages happens after the
+ * final all-reduce of `out`; this form is for callers that own the finished
+ * window (one GPU, or the full window after their own collective).
+ *
+ * Extra arguments (all others as in lt_latent_tail):
+ *   prefix      [T][ld_prefix] bf16, read on the window; 2-byte aligned.
+ *   ld_prefix   row stride of prefix in elements, >= c0 + n.
+ *   resid       [T][ld_resid] bf16, written on the window only; every other
+ *               element is left bit-identical.  May be `prefix` itself (with
+ *               ld_resid == ld_prefix) for an in-place update; must not
+ *               otherwise overlap prefix, and must not overlap partials,
+ *               norm_w, W or out.  prefix must not overlap out.
+ *   ld_resid    row stride of resid in elements, >= c0 + n.
+ *
+ * Returns the codes of lt_latent_tail; LT_ERR_INVALID_ARG also for a NULL
+ * prefix or resid, a stride below c0 + n or an overlap listed above, and
+ * LT_ERR_UNSUPPORTED for an odd address.  T == 0 or n == 0 returns LT_OK
+ * with nothing launched.
+ */
+LT_API int lt_latent_tail_residual(const void *partials, int n_partials, int64_t T, int64_t L,
+                                   const void *norm_w, float eps, const void *W, int64_t H,
+                                   int64_t c0, int64_t n, void *out, int64_t ld_out,
+                                   const void *prefix, int64_t ld_prefix, void *resid,
+                                   int64_t ld_resid, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 LT_API const char *lt_status_string(int status);
 

@@ -46,6 +46,9 @@ def load():
     lib.lt_latent_tail.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_float, vp, i64,
                                    i64, i64, vp, i64, vp]
     lib.lt_latent_tail.restype = ctypes.c_int
+    lib.lt_latent_tail_residual.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_float, vp,
+                                            i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.lt_latent_tail_residual.restype = ctypes.c_int
     lib.lt_status_string.argtypes = [ctypes.c_int]
     lib.lt_status_string.restype = ctypes.c_char_p
     lib.lt_reserve.argtypes = [i64, i64, vp]
@@ -94,6 +97,15 @@ def lt_latent_tail(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld
     return int(load().lt_latent_tail(_ptr(partials), int(n_partials), int(T), int(L),
                                       _ptr(norm_w), float(eps), _ptr(W), int(H), int(c0),
                                       int(n), _ptr(out), int(ld_out), _stream(stream)))
+
+
+def lt_latent_tail_residual(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld_out,
+                            prefix, ld_prefix, resid, ld_resid, stream=None) -> int:
+    """Forward to the C entry point; returns its status code."""
+    return int(load().lt_latent_tail_residual(
+        _ptr(partials), int(n_partials), int(T), int(L), _ptr(norm_w), float(eps), _ptr(W),
+        int(H), int(c0), int(n), _ptr(out), int(ld_out), _ptr(prefix), int(ld_prefix),
+        _ptr(resid), int(ld_resid), _stream(stream)))
 
 
 def lt_status_string(status: int) -> str:

@@ -74,11 +74,12 @@ __device__ __forceinline__ int swz8(int r)
     return ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
 }
 
-template <int BJ, int BT, int WGJ, int WGT, int NS, int GROUP_J, bool KTAIL, bool EPI_LDS>
+template <int BJ, int BT, int WGJ, int WGT, int NS, int GROUP_J, bool KTAIL, bool EPI_LDS, bool RES>
 __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__ Y, int64_t T, int L,
                                                          const u16 *__restrict__ Wn, int n,
                                                          u16 *__restrict__ outn, int64_t ld_out,
-                                                         int ntj, int ntt)
+                                                         int ntj, int ntt, const u16 *prefn,
+                                                         int64_t ld_pre, u16 *resn, int64_t ld_res)
 {
     constexpr int NW = WGJ * WGT;               // waves, in a WGJ x WGT grid
     constexpr int NT = 64 * NW;                 // threads
@@ -379,9 +380,27 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
         constexpr int LPR = CPRE;                    // lanes per tile row
         constexpr int RPI = 64 / LPR;                // rows per store instruction
         static_assert(CPRE <= 64, "row wider than a wave");
-        auto write_back = [&](const char *half, int hh, int wi, int nwv) __attribute__((always_inline)) {
-            const int per = RPH / nwv;
-            for (int i = 0; i < per / RPI; ++i) {
+        // residual: prefix and resid tiles, addressed like `out`
+        const __amdgpu_buffer_rsrc_t rp = lt_rsrc(
+            prefn + t0 * ld_pre, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_pre + n) * 2));
+        const __amdgpu_buffer_rsrc_t rr = lt_rsrc(
+            resn + t0 * ld_res, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_res + n) * 2));
+        auto write_back = [&](const char *half, int hh, int wi, auto NWV) __attribute__((always_inline)) {
+            constexpr int per = RPH / decltype(NWV)::value;
+            constexpr int ITER = per / RPI;
+            // the prefix chunks this lane adds (residual form), all in flight at once
+            u32x4_t pv[RES ? ITER : 1];
+            if constexpr (RES) {
+#pragma unroll
+                for (int i = 0; i < ITER; ++i) {
+                    const int r = hh * RPH + wi * per + i * RPI + l / LPR;
+                    const int j = j0 + 8 * (l % LPR);
+                    pv[i] = lt_buf_load16(rp, j + 8 <= n ? (uint32_t)(((int64_t)r * ld_pre + j) * 2)
+                                                         : LT_OOB);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
                 const int rh = wi * per + i * RPI + l / LPR;
                 const int r = hh * RPH + rh;
                 const int c = l % LPR;
@@ -393,11 +412,29 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
                     if (j + 8 <= n) {
                         __builtin_amdgcn_raw_buffer_store_b128(
                             v, rc, (uint32_t)(((int64_t)r * ld_out + j) * 2), 0, 0);
+                        if constexpr (RES) {
+                            u32x4_t rv;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                rv[e] = lt_pack2(lt_bf_lo(pv[i][e]) + lt_bf_lo(v[e]),
+                                                 lt_bf_hi(pv[i][e]) + lt_bf_hi(v[e]));
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                rv, rr, (uint32_t)(((int64_t)r * ld_res + j) * 2), 0, 0);
+                        }
                     } else {
                         u16 *o = outn + t * ld_out + j;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (j + e < n) o[e] = (u16)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                        for (int e = 0; e < 8; ++e) {
+                            if (j + e < n) {
+                                const u16 onew = (u16)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                                o[e] = onew;
+                                if constexpr (RES) {
+                                    const float rs = lt_bf_lo((uint32_t)prefn[t * ld_pre + j + e]) +
+                                                     lt_bf_lo((uint32_t)onew);
+                                    resn[t * ld_res + j + e] = (u16)(lt_pack2(rs, 0.f) & 0xFFFFu);
+                                }
+                            }
+                        }
                     }
                 }
             }
@@ -409,10 +446,10 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
         // half 1 has landed and half 0 is summed: the half-1 waves sum while
         // the half-0 waves write half 0 back
         if (h == 1) sums(st1);
-        else write_back(st0, 0, wj * (WGT / 2) + wt, NW / 2);
+        else write_back(st0, 0, wj * (WGT / 2) + wt, I<NW / 2>{});
         __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
         lt_lds_barrier();
-        write_back(st1, 1, w, NW);
+        write_back(st1, 1, w, I<NW>{});
     } else {
         // ---- plain epilogue (unaligned `out`): element-wise read-add-round-write
 #pragma unroll
@@ -430,7 +467,13 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
                     for (int e = 0; e < 8; ++e) {
                         if (j + e < n) {
                             const float v = lt_bf_lo((uint32_t)orow[j + e]) + a[8 * hf + e];
-                            orow[j + e] = (u16)(lt_pack2(v, 0.f) & 0xFFFFu);
+                            const u16 onew = (u16)(lt_pack2(v, 0.f) & 0xFFFFu);
+                            orow[j + e] = onew;
+                            if constexpr (RES) {
+                                const float rs = lt_bf_lo((uint32_t)prefn[t * ld_pre + j + e]) +
+                                                 lt_bf_lo((uint32_t)onew);
+                                resn[t * ld_res + j + e] = (u16)(lt_pack2(rs, 0.f) & 0xFFFFu);
+                            }
                         }
                     }
                 }
@@ -441,29 +484,39 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
 
 template <int BJ, int BT, int WGJ, int WGT, int NS, int GROUP_J>
 hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 *outn,
-                      int64_t ld_out, bool vec16, hipStream_t stream)
+                      int64_t ld_out, const Resid *res, bool vec16, hipStream_t stream)
 {
     const int ntj = (n + BJ - 1) / BJ;
     const int64_t ntt = (T + BT - 1) / BT;
     if ((int64_t)ntj * ntt > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(ntj * ntt)), block(64 * WGJ * WGT);
     // The LDS epilogue moves whole out-tile halves with workgroup-wide 16-byte
-    // direct loads and addresses `out` through 32-bit buffer offsets: it needs
-    // an aligned window and a tile extent below 2 GiB; anything else takes the
-    // plain epilogue.
+    // direct loads and addresses `out` (and the residual buffers) through
+    // 32-bit buffer offsets: it needs aligned windows and tile extents below
+    // 2 GiB; anything else takes the plain epilogue.
     constexpr bool EPI_OK = ((BT / 2) * (BJ / 8)) % (64 * WGJ * WGT) == 0;
-    const bool epi = EPI_OK && vec16 && (int64_t)BT * ld_out * 2 < ((int64_t)1 << 31);
-#define LT_GEMM_LAUNCH(KT, EPI)                                                              \
-    hipLaunchKernelGGL((k_gemm<BJ, BT, WGJ, WGT, NS, GROUP_J, KT, EPI>), grid, block, 0, stream, y, T, \
-                       L, Wn, n, outn, ld_out, ntj, (int)ntt)
+    auto small = [&](int64_t ld) { return (int64_t)BT * ld * 2 < ((int64_t)1 << 31); };
+    const bool epi = EPI_OK && vec16 && small(ld_out) &&
+                     (!res || (small(res->ld_prefix) && small(res->ld_resid)));
+    const u16 *pre = res ? res->prefix : nullptr;
+    u16 *rsd = res ? res->resid : nullptr;
+    const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
+#define LT_GEMM_LAUNCH(KT, EPI, R)                                                           \
+    hipLaunchKernelGGL((k_gemm<BJ, BT, WGJ, WGT, NS, GROUP_J, KT, EPI, R>), grid, block, 0, stream, \
+                       y, T, L, Wn, n, outn, ld_out, ntj, (int)ntt, pre, ldp, rsd, ldr)
+#define LT_GEMM_LAUNCH_R(KT, EPI)                                                            \
+    do {                                                                                     \
+        if (res) LT_GEMM_LAUNCH(KT, EPI, true); else LT_GEMM_LAUNCH(KT, EPI, false);        \
+    } while (0)
     const bool kt = L % (NS * BK) != 0;
     if constexpr (EPI_OK) {
         if (epi) {
-            if (kt) LT_GEMM_LAUNCH(true, true); else LT_GEMM_LAUNCH(false, true);
+            if (kt) LT_GEMM_LAUNCH_R(true, true); else LT_GEMM_LAUNCH_R(false, true);
             return hipGetLastError();
         }
     }
-    if (kt) LT_GEMM_LAUNCH(true, false); else LT_GEMM_LAUNCH(false, false);
+    if (kt) LT_GEMM_LAUNCH_R(true, false); else LT_GEMM_LAUNCH_R(false, false);
+#undef LT_GEMM_LAUNCH_R
 #undef LT_GEMM_LAUNCH
     return hipGetLastError();
 }
@@ -471,9 +524,13 @@ hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
-                       uint16_t *outn, int64_t ld_out, hipStream_t stream)
+                       uint16_t *outn, int64_t ld_out, const Resid *res, hipStream_t stream)
 {
-    const bool vec16 = ((reinterpret_cast<uintptr_t>(outn) & 15) == 0) && (ld_out % 8 == 0);
+    auto a16 = [](const void *p, int64_t ld) {
+        return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && ld % 8 == 0;
+    };
+    const bool vec16 = a16(outn, ld_out) && (!res || (a16(res->prefix, res->ld_prefix) &&
+                                                      a16(res->resid, res->ld_resid)));
     // Tile shape and stage count by tile count (measured on n = 7168, T = 128
     // .. 8192, random data): the biggest tile that still gives about one tile
     // per CU.  256 x 256 and 128 x 128 tiles run 8 waves (two per SIMD, which
@@ -481,12 +538,12 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
     // four stages in flight hide the L2 latency that two stages leave exposed.
     auto tiles = [&](int bj, int bt) { return (int64_t)((n + bj - 1) / bj) * ((T + bt - 1) / bt); };
     if (tiles(256, 256) >= 224)
-        return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+        return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     if (tiles(128, 128) >= 448)
-        return launch_cfg<128, 128, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+        return launch_cfg<128, 128, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     if (tiles(128, 128) >= 224)
-        return launch_cfg<128, 128, 4, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
-    return launch_cfg<64, 128, 2, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, vec16, stream);
+        return launch_cfg<128, 128, 4, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
+    return launch_cfg<64, 128, 2, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
 }
 
 }  // namespace lt

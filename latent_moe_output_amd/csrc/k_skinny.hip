@@ -36,13 +36,14 @@
 namespace lt {
 namespace {
 
-template <int NI, int TT, int JT>
+template <int NI, int TT, int JT, bool RES>
 __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part, int64_t pstride,
                                                     int P, int T, int L,
                                                     const u16 *__restrict__ norm_w, float eps,
                                                     float inv_L, const u16 *__restrict__ Wn, int n,
                                                     int RW, u16 *__restrict__ outn, int64_t ld_out,
-                                                    int vec8)
+                                                    int vec8, const u16 *prefn, int64_t ld_pre,
+                                                    u16 *resn, int64_t ld_res)
 {
     static_assert(JT * TT <= KW, "one epilogue fragment per wave");
     const int l = threadIdx.x & 63;
@@ -84,8 +85,11 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
     const int tte = w % TT, jte = w / TT;
     const int te = 16 * tte + r, jl = 16 * jte + 4 * g;   // token, local row
     const bool out_vec = has_epi && te < T && vec8 && jl + 4 <= rows;
-    u32x2_t opre = {0u, 0u};
-    if (out_vec) opre = *reinterpret_cast<const u32x2_t *>(outn + (int64_t)te * ld_out + j0 + jl);
+    u32x2_t opre = {0u, 0u}, ppre = {0u, 0u};
+    if (out_vec) {
+        opre = *reinterpret_cast<const u32x2_t *>(outn + (int64_t)te * ld_out + j0 + jl);
+        if constexpr (RES) ppre = *reinterpret_cast<const u32x2_t *>(prefn + (int64_t)te * ld_pre + j0 + jl);
+    }
 
     // 2. RMSNorm (its barrier waits for LDS only; W stays in flight)
     if (norm_w) {
@@ -127,12 +131,26 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
         nv[0] = lt_pack2(lt_bf_lo(opre[0]) + d[0], lt_bf_hi(opre[0]) + d[1]);
         nv[1] = lt_pack2(lt_bf_lo(opre[1]) + d[2], lt_bf_hi(opre[1]) + d[3]);
         *reinterpret_cast<u32x2_t *>(o) = nv;
+        if constexpr (RES) {
+            u32x2_t rv;
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                rv[e] = lt_pack2(lt_bf_lo(ppre[e]) + lt_bf_lo(nv[e]), lt_bf_hi(ppre[e]) + lt_bf_hi(nv[e]));
+            *reinterpret_cast<u32x2_t *>(resn + (int64_t)te * ld_res + j0 + jl) = rv;
+        }
     } else {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             if (jl + a < rows) {
                 const float v = lt_bf_lo((uint32_t)o[a]) + d[a];
-                o[a] = (u16)(lt_pack2(v, 0.f) & 0xFFFFu);
+                const u16 onew = (u16)(lt_pack2(v, 0.f) & 0xFFFFu);
+                o[a] = onew;
+                if constexpr (RES) {
+                    const int64_t jj = j0 + jl + a;
+                    const float r = lt_bf_lo((uint32_t)prefn[(int64_t)te * ld_pre + jj]) +
+                                    lt_bf_lo((uint32_t)onew);
+                    resn[(int64_t)te * ld_res + jj] = (u16)(lt_pack2(r, 0.f) & 0xFFFFu);
+                }
             }
         }
     }
@@ -150,42 +168,48 @@ int rows_per_block(int n)
 template <int NI, int TT, int JT>
 hipError_t launch_nt(const u16 *part, int64_t pstride, int P, int T, int L, const u16 *norm_w,
                      float eps, const u16 *Wn, int n, int RW, u16 *outn, int64_t ld_out, int vec8,
-                     hipStream_t stream)
+                     const Resid *res, hipStream_t stream)
 {
     const dim3 grid((n + RW - 1) / RW), block(64 * KW);
-    hipLaunchKernelGGL((k_skinny<NI, TT, JT>), grid, block, 0, stream, part, pstride, P, T, L,
-                       norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8);
+    if (res)
+        hipLaunchKernelGGL((k_skinny<NI, TT, JT, true>), grid, block, 0, stream, part, pstride, P,
+                           T, L, norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8,
+                           res->prefix, res->ld_prefix, res->resid, res->ld_resid);
+    else
+        hipLaunchKernelGGL((k_skinny<NI, TT, JT, false>), grid, block, 0, stream, part, pstride,
+                           P, T, L, norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8,
+                           nullptr, (int64_t)0, nullptr, (int64_t)0);
     return hipGetLastError();
 }
 
 template <int NI, int JT>
 hipError_t launch_jt(const u16 *part, int64_t pstride, int P, int T, int L, const u16 *norm_w,
                      float eps, const u16 *Wn, int n, int RW, u16 *outn, int64_t ld_out, int vec8,
-                     hipStream_t stream)
+                     const Resid *res, hipStream_t stream)
 {
     if (T <= 16)
         return launch_nt<NI, 1, JT>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out,
-                                    vec8, stream);
+                                    vec8, res, stream);
     if (T <= 32)
         return launch_nt<NI, 2, JT>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out,
-                                    vec8, stream);
+                                    vec8, res, stream);
     if constexpr (NI <= 4)
         return launch_nt<NI, 4, JT>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out,
-                                    vec8, stream);
+                                    vec8, res, stream);
     return hipErrorInvalidValue;
 }
 
 template <int NI>
 hipError_t launch_ni(const u16 *part, int64_t pstride, int P, int T, int L, const u16 *norm_w,
                      float eps, const u16 *Wn, int n, u16 *outn, int64_t ld_out, int vec8,
-                     hipStream_t stream)
+                     const Resid *res, hipStream_t stream)
 {
     const int RW = rows_per_block(n);
     if (RW <= 16)
         return launch_jt<NI, 1>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out,
-                                vec8, stream);
+                                vec8, res, stream);
     return launch_jt<NI, 2>(part, pstride, P, T, L, norm_w, eps, Wn, n, RW, outn, ld_out, vec8,
-                            stream);
+                            res, stream);
 }
 
 }  // namespace
@@ -194,15 +218,19 @@ int skinny_tokens_per_launch(int L) { return latent_steps(L) > 4 ? 32 : 64; }
 
 hipError_t launch_skinny(const uint16_t *part, int64_t pstride, int P, int T, int L,
                          const uint16_t *norm_w, float eps, const uint16_t *Wn, int n,
-                         uint16_t *outn, int64_t ld_out, hipStream_t stream)
+                         uint16_t *outn, int64_t ld_out, const Resid *res, hipStream_t stream)
 {
     if (T < 1 || T > skinny_tokens_per_launch(L)) return hipErrorInvalidValue;
-    const int vec8 = ((reinterpret_cast<uintptr_t>(outn) & 7) == 0) && (ld_out % 4 == 0);
+    auto a8 = [](const void *p, int64_t ld) {
+        return (reinterpret_cast<uintptr_t>(p) & 7) == 0 && ld % 4 == 0;
+    };
+    const int vec8 = a8(outn, ld_out) && (!res || (a8(res->prefix, res->ld_prefix) &&
+                                                   a8(res->resid, res->ld_resid)));
     const int ni = latent_steps(L);
-    if (ni <= 1) return launch_ni<1>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
-    if (ni <= 2) return launch_ni<2>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
-    if (ni <= 4) return launch_ni<4>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
-    return launch_ni<8>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, stream);
+    if (ni <= 1) return launch_ni<1>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, res, stream);
+    if (ni <= 2) return launch_ni<2>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, res, stream);
+    if (ni <= 4) return launch_ni<4>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, res, stream);
+    return launch_ni<8>(part, pstride, P, T, L, norm_w, eps, Wn, n, outn, ld_out, vec8, res, stream);
 }
 
 }  // namespace lt

@@ -182,9 +182,15 @@ int lt_release_scratch(void)
     return LT_OK;
 }
 
-int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
-                   const void *norm_w, float eps, const void *W, int64_t H, int64_t c0,
-                   int64_t n, void *out, int64_t ld_out, void *stream)
+}  // extern "C"
+
+namespace {
+
+// The tail, with the residual update when `res` is set (its pointers
+// validated by the caller and not yet offset by c0).
+int tail_impl(const void *partials, int n_partials, int64_t T, int64_t L, const void *norm_w,
+              float eps, const void *W, int64_t H, int64_t c0, int64_t n, void *out,
+              int64_t ld_out, const lt::Resid *res_in, void *stream)
 {
     // ---- sizes and window
     if (n_partials < 1 || T < 0 || L < 1 || H < 1 || c0 < 0 || n < 0 || c0 > H || n > H - c0 ||
@@ -214,6 +220,32 @@ int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
         ranges_overlap(out, out_bytes, norm_w, (size_t)L * 2))
         return LT_ERR_INVALID_ARG;
 
+    // ---- the residual buffers: prefix is read, resid written (resid may be
+    // the prefix buffer itself, with the same stride)
+    lt::Resid res_win{};
+    const lt::Resid *res = nullptr;
+    if (res_in) {
+        const lt::Resid &r = *res_in;
+        if (!r.prefix || !r.resid || r.ld_prefix < c0 + n || r.ld_resid < c0 + n)
+            return LT_ERR_INVALID_ARG;
+        int64_t tp = 0, tr = 0;
+        if (!mul_ok(T - 1, r.ld_prefix, &tp) || !mul_ok(T - 1, r.ld_resid, &tr) ||
+            tp > INT64_MAX / 4 || tr > INT64_MAX / 4)
+            return LT_ERR_INVALID_ARG;
+        if (!aligned(r.prefix, 2) || !aligned(r.resid, 2)) return LT_ERR_UNSUPPORTED;
+        const size_t pb = (size_t)(tp + c0 + n) * 2, rb = (size_t)(tr + c0 + n) * 2;
+        const size_t ob = (size_t)(tld + H) * 2;
+        const bool same = r.resid == r.prefix && r.ld_resid == r.ld_prefix;
+        if (ranges_overlap(r.resid, rb, partials, (size_t)ptl * 2) ||
+            ranges_overlap(r.resid, rb, W, (size_t)hl * 2) ||
+            ranges_overlap(r.resid, rb, norm_w, (size_t)L * 2) ||
+            ranges_overlap(r.resid, rb, out, ob) || ranges_overlap(r.prefix, pb, out, ob) ||
+            (!same && ranges_overlap(r.resid, rb, r.prefix, pb)))
+            return LT_ERR_INVALID_ARG;
+        res_win = {r.prefix + c0, r.ld_prefix, r.resid + c0, r.ld_resid};
+        res = &res_win;
+    }
+
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const uint16_t *part = static_cast<const uint16_t *>(partials);
     const uint16_t *nw = static_cast<const uint16_t *>(norm_w);
@@ -226,8 +258,13 @@ int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
         if (!record_hook(g_ev_before, s)) return LT_ERR_HIP;
         for (int64_t tb = 0; tb < T; tb += per) {
             const int tc = (int)((T - tb) < per ? (T - tb) : per);
+            lt::Resid rb{};
+            if (res)
+                rb = {res->prefix + tb * res->ld_prefix, res->ld_prefix,
+                      res->resid + tb * res->ld_resid, res->ld_resid};
             hipError_t e = lt::launch_skinny(part + tb * L, tl, n_partials, tc, (int)L, nw, eps,
-                                             Wn, (int)n, outn + tb * ld_out, ld_out, s);
+                                             Wn, (int)n, outn + tb * ld_out, ld_out,
+                                             res ? &rb : nullptr, s);
             if (e != hipSuccess) return LT_ERR_HIP;
         }
         return record_hook(g_ev_after, s) ? LT_OK : LT_ERR_HIP;
@@ -240,9 +277,32 @@ int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
     if (lt::launch_sum_rmsnorm(part, tl, n_partials, T, (int)L, nw, eps, y, s) != hipSuccess)
         return LT_ERR_HIP;
     if (!record_hook(g_ev_before, s)) return LT_ERR_HIP;
-    if (lt::launch_gemm(y, T, (int)L, Wn, (int)n, outn, ld_out, s) != hipSuccess)
+    if (lt::launch_gemm(y, T, (int)L, Wn, (int)n, outn, ld_out, res, s) != hipSuccess)
         return LT_ERR_HIP;
     return record_hook(g_ev_after, s) ? LT_OK : LT_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
+                   const void *norm_w, float eps, const void *W, int64_t H, int64_t c0,
+                   int64_t n, void *out, int64_t ld_out, void *stream)
+{
+    return tail_impl(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld_out, nullptr,
+                     stream);
+}
+
+int lt_latent_tail_residual(const void *partials, int n_partials, int64_t T, int64_t L,
+                            const void *norm_w, float eps, const void *W, int64_t H, int64_t c0,
+                            int64_t n, void *out, int64_t ld_out, const void *prefix,
+                            int64_t ld_prefix, void *resid, int64_t ld_resid, void *stream)
+{
+    const lt::Resid r{static_cast<const uint16_t *>(prefix), ld_prefix,
+                      static_cast<uint16_t *>(resid), ld_resid};
+    return tail_impl(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld_out, &r,
+                     stream);
 }
 
 }  // extern "C"

@@ -11,11 +11,21 @@
 
 namespace lt {
 
+// Optional residual update after the tail: resid[t][j] = bf16(prefix[t][j] +
+// out'[t][j]) on the window (pointers already offset by c0, row strides in
+// elements).  resid may equal prefix (same stride).
+struct Resid {
+    const uint16_t *prefix;
+    int64_t ld_prefix;
+    uint16_t *resid;
+    int64_t ld_resid;
+};
+
 // Weight-streaming path: fused partial sum + RMSNorm + projection +
 // beta-add for tokens [0, T) of `part` (T <= 64; partial stride `pstride`).
 hipError_t launch_skinny(const uint16_t *part, int64_t pstride, int P, int T, int L,
                          const uint16_t *norm_w, float eps, const uint16_t *Wn, int n,
-                         uint16_t *outn, int64_t ld_out, hipStream_t stream);
+                         uint16_t *outn, int64_t ld_out, const Resid *res, hipStream_t stream);
 
 // Largest token count one skinny launch handles for latent width L.
 int skinny_tokens_per_launch(int L);
@@ -25,8 +35,9 @@ hipError_t launch_sum_rmsnorm(const uint16_t *part, int64_t pstride, int P, int6
                               int L, const uint16_t *norm_w, float eps, uint16_t *y,
                               hipStream_t stream);
 
-// out[t][j] = bf16(out[t][j] + sum_k y[t][k] * Wn[j][k]) for t < T, j < n.
+// out[t][j] = bf16(out[t][j] + sum_k y[t][k] * Wn[j][k]) for t < T, j < n
+// (and the residual update when res is not NULL).
 hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
-                       uint16_t *outn, int64_t ld_out, hipStream_t stream);
+                       uint16_t *outn, int64_t ld_out, const Resid *res, hipStream_t stream);
 
 }  // namespace lt

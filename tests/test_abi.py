@@ -119,3 +119,35 @@ def test_reserve_rejects_bad_sizes(lib):
     assert binding.lt_reserve(-1, 1024) == binding.LT_ERR_INVALID_ARG
     assert binding.lt_reserve(4, 0) == binding.LT_ERR_INVALID_ARG
     assert binding.lt_reserve(0, 1024) == binding.LT_OK
+
+
+# residual form: its extra arguments are validated before anything launches
+_RES_BASE = dict(partials=FAKE, n_partials=1, T=16, L=1024, norm_w=FAKE + (1 << 30), eps=1e-6,
+                 W=FAKE + (1 << 20), H=7168, c0=8, n=7000, out=FAKE + (1 << 31), ld_out=7168,
+                 prefix=FAKE + (1 << 33), ld_prefix=7168, resid=FAKE + (1 << 34),
+                 ld_resid=7168)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(prefix=None), binding.LT_ERR_INVALID_ARG),
+    (dict(resid=None), binding.LT_ERR_INVALID_ARG),
+    (dict(ld_prefix=7007), binding.LT_ERR_INVALID_ARG),          # below c0 + n
+    (dict(ld_resid=7007), binding.LT_ERR_INVALID_ARG),
+    (dict(prefix=FAKE + (1 << 33) + 1), binding.LT_ERR_UNSUPPORTED),
+    (dict(resid=FAKE + (1 << 34) + 1), binding.LT_ERR_UNSUPPORTED),
+    (dict(resid=FAKE + (1 << 31) + 64), binding.LT_ERR_INVALID_ARG),   # resid inside out
+    (dict(prefix=FAKE + (1 << 31)), binding.LT_ERR_INVALID_ARG),       # prefix is out
+    (dict(resid=FAKE + (1 << 20)), binding.LT_ERR_INVALID_ARG),        # resid inside W
+    (dict(resid=FAKE), binding.LT_ERR_INVALID_ARG),                    # resid is partials
+    (dict(resid=FAKE + (1 << 33) + 2), binding.LT_ERR_INVALID_ARG),    # shifted onto prefix
+    (dict(resid=FAKE + (1 << 33), ld_resid=7176), binding.LT_ERR_INVALID_ARG),  # same base, other stride
+    (dict(eps=-1.0), binding.LT_ERR_INVALID_ARG),                      # the tail's own checks
+    (dict(L=1000 + 4), binding.LT_ERR_UNSUPPORTED),
+])
+def test_residual_invalid_arguments_are_rejected(lib, kw, code):
+    assert binding.lt_latent_tail_residual(**dict(_RES_BASE, **kw)) == code
+
+
+def test_residual_empty_calls_launch_nothing(lib):
+    assert binding.lt_latent_tail_residual(**dict(_RES_BASE, T=0)) == binding.LT_OK
+    assert binding.lt_latent_tail_residual(**dict(_RES_BASE, n=0)) == binding.LT_OK
