@@ -22,16 +22,16 @@ __global__ __launch_bounds__(64 * KW) void k_sum_rmsnorm(const u16 *__restrict__
                                                          const u16 *__restrict__ norm_w, float eps,
                                                          float inv_L, u16 *__restrict__ y)
 {
-    __shared__ float red[KW * 16];
+    __shared__ float red[1][KW * 16];
     const int64_t t0 = (int64_t)blockIdx.x * 16;
     const int Tv = (int)min((int64_t)16, T - t0);
     const u16 *tile = part + t0 * L;
 
-    u32x4_t sv[NI], wv[NI];
-    latent_load(tile, Tv, L, sv);
+    u32x4_t sv[1][NI], wv[NI];
+    latent_load(tile, Tv, L, sv[0]);
     if (norm_w) latent_load_weight(norm_w, L, wv);
-    latent_sum(tile, pstride, P, Tv, L, sv);
-    if (norm_w) latent_norm(sv, wv, eps, inv_L, red);
+    latent_sum(tile, pstride, P, Tv, L, sv[0]);
+    if (norm_w) latent_norm<1, NI>(sv, wv, eps, inv_L, red);
 
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t = l & 15, g = l >> 4;
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(64 * KW) void k_sum_rmsnorm(const u16 *__restrict__
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int c = 4 * KW * i + 4 * w + g;
-        if (c < nchunk) *reinterpret_cast<u32x4_t *>(row + c * 8) = sv[i];
+        if (c < nchunk) *reinterpret_cast<u32x4_t *>(row + c * 8) = sv[0][i];
     }
 }
 

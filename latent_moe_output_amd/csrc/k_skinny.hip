@@ -92,10 +92,7 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
     }
 
     // 2. RMSNorm (its barrier waits for LDS only; W stays in flight)
-    if (norm_w) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) latent_norm(sv[tt], wv, eps, inv_L, red_ss[tt]);
-    }
+    if (norm_w) latent_norm<TT, NI>(sv, wv, eps, inv_L, red_ss);
 
     // 3. projection on the matrix cores: D[j][t] += W[j][k] * y[t][k]
     f32x4_t acc[JT][TT];

@@ -100,34 +100,40 @@ __device__ __forceinline__ void latent_sum(const u16 *__restrict__ tile, int64_t
     for (int i = 0; i < NI; ++i) sv[i] = lt_pack8(s[i]);
 }
 
-// RMSNorm of the tile in place: y = bf16((s * rsqrt(mean(s^2) + eps)) * w).
-// `red` is LDS scratch of KW * 16 floats.  Contains a workgroup barrier:
-// every thread of the workgroup must call it.
-template <int NI>
-__device__ __forceinline__ void latent_norm(u32x4_t (&sv)[NI], const u32x4_t (&wv)[NI],
-                                            float eps, float inv_L, float *red)
+// RMSNorm of TT tiles in place: y = bf16((s * rsqrt(mean(s^2) + eps)) * w).
+// `red` is LDS scratch of TT * KW * 16 floats.  One workgroup barrier for all
+// tiles: every thread of the workgroup must call it.
+template <int TT, int NI>
+__device__ __forceinline__ void latent_norm(u32x4_t (&sv)[TT][NI], const u32x4_t (&wv)[NI],
+                                            float eps, float inv_L, float (*red)[KW * 16])
 {
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t = l & 15;
-    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const bf16x8_t s = __builtin_bit_cast(bf16x8_t, sv[i]);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s, s, d, 0, 0, 0);
+    for (int tt = 0; tt < TT; ++tt) {
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const bf16x8_t s = __builtin_bit_cast(bf16x8_t, sv[tt][i]);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s, s, d, 0, 0, 0);
+        }
+        // D[t][t] sits in lane 16*(t/4) + t, element t % 4
+        if ((l >> 4) == (t >> 2)) red[tt][w * 16 + t] = d[t & 3];
     }
-    // D[t][t] sits in lane 16*(t/4) + t, element t % 4
-    if ((l >> 4) == (t >> 2)) red[w * 16 + t] = d[t & 3];
     __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));   // LDS only: loads may stay in flight
     lt_lds_barrier();
-    float total = red[t];
 #pragma unroll
-    for (int v = 1; v < KW; ++v) total = total + red[v * 16 + t];
-    const float rs = lt_inv_rms(total, inv_L, eps);
+    for (int tt = 0; tt < TT; ++tt) {
+        float total = red[tt][t];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        float s[8];
-        lt_unpack8(sv[i], s);
-        sv[i] = lt_scale_chunk(s, rs, wv[i]);
+        for (int v = 1; v < KW; ++v) total = total + red[tt][v * 16 + t];
+        const float rs = lt_inv_rms(total, inv_L, eps);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float s[8];
+            lt_unpack8(sv[tt][i], s);
+            sv[tt][i] = lt_scale_chunk(s, rs, wv[i]);
+        }
     }
 }
 
