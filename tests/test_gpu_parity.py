@@ -108,23 +108,27 @@ def test_large_workload_sampled(name):
     assert np.array_equal(got[outside], d["out"][outside])
 
 
-@pytest.mark.parametrize("T,n,c0,ld,P", [
-    (2000, 7100, 37, 7168, 2),   # 256 x 256 tiles, 2 stages (224 tiles), ragged both ways
-    (1000, 7100, 5, 7120, 1),    # 128 x 128 tiles, 2 stages
-    (500, 7100, 11, 7128, 3),    # 128 x 128 tiles, 4 stages
-    (300, 3000, 8, 3016, 1),     # 64 x 128 tiles, 4 waves, 4 stages
+@pytest.mark.parametrize("T,n,c0,ld,P,L", [
+    (2000, 7100, 37, 7168, 2, 1024),   # 256 x 256 tiles, 2 stages (224 tiles), ragged both ways
+    (1000, 7100, 5, 7120, 1, 1024),    # 128 x 128 tiles, 2 stages
+    (500, 7100, 11, 7128, 3, 1024),    # 128 x 128 tiles, 4 stages
+    (300, 3000, 8, 3016, 1, 1024),     # 64 x 128 tiles, 4 waves, 4 stages
+    (2000, 7100, 64, 7168, 1, 1032),   # 256 x 256, LDS epilogue, K tail (L % 128 != 0)
+    (1000, 7100, 32, 7136, 2, 1096),   # 128 x 128 / 2 stages with a K tail
+    (500, 7100, 0, 7104, 1, 1160),     # 128 x 128 / 4 stages with a K tail
+    (1500, 4000, 0, 4008, 1, 2048),    # widest latent, 128 x 128 / 4 stages
 ])
-def test_gemm_tile_shapes_sampled(T, n, c0, ld, P):
+def test_gemm_tile_shapes_sampled(T, n, c0, ld, P, L):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
     offset window: oracle on sampled rows (tile edges included, all window
     columns), untouched elements over the whole buffer."""
     from oracle import oracle
 
-    wl = synth.Workload("tiles", T=T, L=1024, H=c0 + n + 3, P=P, c0=c0, n=n, ld_out=ld,
+    wl = synth.Workload("tiles", T=T, L=L, H=c0 + n + 3, P=P, c0=c0, n=n, ld_out=ld,
                         part_std=0.6)
     d = synth.generate(wl, seed=T + n)
     di = DevInputs(d)
-    say("case tiles T=%d n=%d c0=%d ld=%d P=%d" % (T, n, c0, ld, P))
+    say("case tiles T=%d n=%d c0=%d ld=%d P=%d L=%d" % (T, n, c0, ld, P, L))
     assert binding.lt_path_for(T, n) == 2
     binding.check(di.call(wl))
     _sync()

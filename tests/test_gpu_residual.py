@@ -166,3 +166,45 @@ def test_plain_and_residual_forms_give_the_same_out():
 
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(a.out), host(b.out))
+
+
+@pytest.mark.parametrize("T", [8, 700])
+def test_residual_graph_capture_and_replay(T):
+    """The residual form captured into a HIP graph (after lt_reserve) and
+    replayed with eager work between replays: every replay matches eager."""
+    import torch
+
+    wl = synth.Workload("res_graph", T=T, L=1024, H=2048, P=2, c0=256, n=1536, ld_out=2048,
+                        part_std=0.6)
+    d = synth.generate(wl, seed=5)
+    prefix, resid0 = _res_inputs(wl, 2048, 2048, seed=6)
+    di = DevInputs(d)
+    pd, rd = dev(prefix), dev(resid0)
+    say("graph residual eager T=%d" % T)
+    binding.check(_call(di, wl, pd, 2048, rd, 2048))
+    torch.cuda.synchronize()
+    want_out, want_res = host(di.out), host(rd)
+
+    s = torch.cuda.Stream()
+    assert binding.lt_reserve(T, wl.L, s) == binding.LT_OK
+    g = torch.cuda.CUDAGraph()
+    rd0 = dev(resid0)
+    di.reset_out()
+    rd.copy_(rd0)
+    torch.cuda.synchronize()
+    say("graph residual capture T=%d" % T)
+    with torch.cuda.graph(g, stream=s):
+        status = _call(di, wl, pd, 2048, rd, 2048, stream=torch.cuda.current_stream())
+    assert status == binding.LT_OK
+    for rep in range(3):
+        di.reset_out()
+        rd.copy_(rd0)
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        say("graph residual replay %d T=%d" % (rep, T))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(di.out), want_out)
+        np.testing.assert_array_equal(host(rd), want_res)
+        del junk
+    del g
