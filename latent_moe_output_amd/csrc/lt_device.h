@@ -16,9 +16,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// One 8-element chunk (16 bytes) of a bf16 row.
-#define LT_CHUNK 8
-
 __device__ __forceinline__ float lt_bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float lt_bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
@@ -45,11 +42,6 @@ __device__ __forceinline__ u32x4_t lt_pack8(const float f[8])
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = lt_pack2(f[2 * i], f[2 * i + 1]);
     return v;
-}
-
-__device__ __forceinline__ u32x4_t lt_load16(const u16 *p)
-{
-    return *reinterpret_cast<const u32x4_t *>(p);
 }
 
 // Raw buffer resources (stride 0): a load whose byte offset is at or past
