@@ -12,11 +12,11 @@
 //    v_mfma_f32_32x32x16_bf16 with W as the A operand and the latent as B.
 //  * K advances 64 at a time through NS (2 or 4) LDS stages filled straight
 //    from L2 by buffer_load_dwordx4 ... lds: while one stage is multiplied
-//    the next NS-1 are in flight.  A stage row is 64 bf16 = one whole 128-byte line of
-//    the operand row, the unit the L2 hands out; half-line slices (32 bf16)
-//    measured at half the fill rate.  Buffer resources are clipped per
-//    workgroup: rows past the end of W's window or past T read as zero with
-//    no branch.
+//    the next NS-1 are in flight.  A stage row is 64 bf16 = one whole
+//    128-byte line of the operand row, the unit the L2 hands out; half-line
+//    slices (32 bf16) measured at half the fill rate.  Buffer resources are
+//    clipped per workgroup: rows past the end of W's window or past T read as
+//    zero with no branch.
 //  * Each direct load writes 1 KB (8 rows) contiguously; the 16-byte chunk a
 //    lane fetches is chosen so the rows land XOR-swizzled (key swz8).
 //    Fragments of both operands are read from rows perm32(lane % 32) of each
@@ -30,9 +30,12 @@
 //  * Epilogue: the `out` tile moves through LDS in two halves of token rows,
 //    fetched into stage arrays as soon as the K loop frees them (with two
 //    stages: half 0 during the last K stage, half 1 once the MFMAs are done,
-//    while the waves owning half 0 form their sums).  Sums are rounded once in place and the tile is
-//    written back row by row, so every store covers whole contiguous row
-//    segments of `out`.
+//    while the waves owning half 0 form their sums).  Sums are rounded once
+//    in place and the tile is written back row by row, so every store covers
+//    whole contiguous row segments of `out`.  The residual form (RES) adds
+//    the prefix chunks to the rounded rows on the way out and stores the
+//    residual the same way ([PR50593 Key source snippets,
+//    `forward_attn_residual`]: the layer's post-MLP prefix-sum update).
 //  * Ragged edges are masked on store; nothing outside [c0, c0+n) x [0, T) is
 //    written.
 //  * Tiles are spread so that each of the 8 XCDs receives a contiguous range

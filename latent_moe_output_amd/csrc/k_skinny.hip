@@ -15,10 +15,12 @@
 //    are loaded straight into registers in the A-operand layout of
 //    v_mfma_f32_16x16x32_bf16 (row = lane % 16, 8 consecutive k per lane), so
 //    W never passes through LDS.
-//  * The partial chunks are loaded first, then the norm weight, then all of
-//    the workgroup's W chunks, then the out values the epilogue will add to:
-//    the whole W share is in flight while the latent is normalised, and the
-//    read-modify-write of the window adds no memory round trip at the end.
+//  * The partial chunks are loaded first (and, with several partials, summed
+//    before anything else is issued, so the sum's waits never drain the W
+//    stream), then the norm weight, then all of the workgroup's W chunks,
+//    then the out values the epilogue will add to: the whole W share is in
+//    flight while the latent is normalised, and the read-modify-write of the
+//    window adds no memory round trip at the end.
 //  * The latent is built in registers in the B-operand layout (token = lane
 //    % 16) by the shared tile code of lt_latent.h; splitting K over KW waves
 //    keeps each lane's share of the RMSNorm arithmetic small, and the norm's
@@ -26,7 +28,9 @@
 //    dimension; the idle columns of a partly filled token tile cost nothing
 //    that matters here, the matrix cores are far from busy.
 //  * The KW per-wave partial products are added in LDS in wave order and
-//    written with one bf16 rounding onto the window.
+//    written with one bf16 rounding onto the window.  The residual form (RES)
+//    also writes bf16(prefix + out') with the prefix prefetched alongside
+//    `out` ([PR50593 Key source snippets, `forward_attn_residual`]).
 //
 // Every element's accumulation order depends only on (T, L), never on c0 or
 // n, so column shards reproduce the full-window result bit for bit.

@@ -5,8 +5,11 @@
 // narrow W rows and out columns to [c0, c0+n), add the projection in place.
 // The token-count dispatcher mirrors the tier choice of [PR50383
 // Implementation, item 1], reduced to the two single-GPU paths:
-//   T <= skinny_max  -> one weight-streaming launch per 64 tokens (k_skinny)
+//   T <= skinny_max  -> one weight-streaming launch per 64 tokens (32 when
+//                       L > 1024) (k_skinny)
 //   T >  skinny_max  -> k_sum_rmsnorm into a scratch latent, then k_gemm.
+// lt_latent_tail_residual runs the same path with the decoder layer's
+// residual update fused into the epilogue of the projection kernel.
 // The pages' own fallback is silent ([PR51253 Implementation, item 2]); a
 // library cannot fall back to a path it does not own, so every violated
 // precondition is an explicit status code returned before any launch.
