@@ -130,6 +130,48 @@ def gemm_traffic_bytes():
 RES_T = [1, 16, 1024, 8192]
 
 
+def context_pass(binding, hip, stream, sh, sets, wpool, norm_w, reps=20):
+    """Context for the roofline fractions, not part of `value`: the copy
+    bandwidth this GPU reaches on a W-sized buffer (PyTorch device copy), and
+    warm timings (the same W, partials and out every call, so W stays in the
+    256 MB Infinity Cache) next to the cold ones."""
+    import numpy as np
+    import torch
+
+    ctx = {}
+    with torch.cuda.stream(stream):
+        a, b = hip.event(), hip.event()
+        big = [torch.empty(64 << 20, dtype=torch.int16, device="cuda") for _ in range(2)]
+        for _ in range(3):
+            big[1].copy_(big[0])
+        hip.record(a, sh)
+        for i in range(reps):
+            big[(i + 1) % 2].copy_(big[i % 2])
+        hip.record(b, sh)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(a, b) * 1e3 / reps
+        ctx["copy_128MiB"] = {"us": round(us, 2),
+                              "gbps_read_plus_write": round(2 * big[0].numel() * 2 / us / 1e3, 1)}
+        del big
+        warm = {}
+        for T in (1, 8192):
+            p, o = sets[T][0]
+            W = wpool[0]
+            for _ in range(3):
+                binding.check(binding.lt_latent_tail(p, P, T, L, norm_w, EPS, W, H, 0, H, o, H, sh))
+            hip.record(a, sh)
+            for _ in range(reps):
+                binding.check(binding.lt_latent_tail(p, P, T, L, norm_w, EPS, W, H, 0, H, o, H, sh))
+            hip.record(b, sh)
+            torch.cuda.synchronize()
+            warm[str(T)] = {"call_us": round(hip.elapsed_ms(a, b) * 1e3 / reps, 3),
+                            "timing": "%d back-to-back calls" % reps}
+        ctx["warm_same_buffers"] = warm
+        hip.destroy(a)
+        hip.destroy(b)
+    return ctx
+
+
 def residual_pass(binding, hip, stream, sh, sets, wpool, norm_w, call_kern, reps=20):
     """The residual form (the tail plus the decoder layer's prefix-sum update,
     fused into the epilogue) against the unfused pair: the tail, then a
@@ -192,6 +234,14 @@ def cpu_baseline(d, target_s=12.0):
     t0 = time.perf_counter()
     oracle.latent_tail(d["partials"][:, :S], d["norm_w"], EPS, d["W"], 0, H, d["out"][:S])
     dt = time.perf_counter() - t0
+    # the same oracle on one thread, on a sample a sixteenth the size
+    S1 = max(16, (S // 16) // 16 * 16)
+    t0 = time.perf_counter()
+    oracle.latent_tail(d["partials"][:, :S1], d["norm_w"], EPS, d["W"], 0, H, d["out"][:S1],
+                       nthreads=1)
+    dt1 = time.perf_counter() - t0
+    oracle.latent_tail(d["partials"][:, :16], d["norm_w"], EPS, d["W"], 0, H, d["out"][:16],
+                       nthreads=threads)                       # restore the thread count
     return {
         "value": flops_of(S) / dt / 1e12,
         "unit": "TFLOP/s",
@@ -201,7 +251,21 @@ def cpu_baseline(d, target_s=12.0):
                   "partial, RMSNorm on), fp64 C oracle, %d OpenMP threads, %.2f s" % (S, threads, dt),
         "seconds": dt,
         "tokens": S,
+        "cpu_model": cpu_model(),
+        "single_thread": {"value": flops_of(S1) / dt1 / 1e12, "unit": "TFLOP/s",
+                          "tokens": S1, "seconds": dt1},
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -349,6 +413,7 @@ def main():
                 hip.destroy(e)
 
     residual = residual_pass(binding, hip, stream, sh, sets, wpool, norm_w, call_kern=kern_us)
+    context = context_pass(binding, hip, stream, sh, sets, wpool, norm_w)
 
     total_flops = K * sum(flops_of(T) for T in T_SWEEP)
     total_w = K * nT * 2 * H * L
@@ -424,6 +489,7 @@ def main():
         "roofline": roofline,
         "roofline_skinny": roofline_skinny,
         "residual": residual,
+        "context": context,
     }
     if not args.no_cpu:
         log("timing the CPU oracle ...")
