@@ -388,20 +388,26 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
             prefn + t0 * ld_pre, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_pre + n) * 2));
         const __amdgpu_buffer_rsrc_t rr = lt_rsrc(
             resn + t0 * ld_res, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_res + n) * 2));
-        auto write_back = [&](const char *half, int hh, int wi, auto NWV) __attribute__((always_inline)) {
+        // rows [wi*per, (wi+1)*per) of half hh, per = RPH / NWV, go out in
+        // per / RPI store rounds; the residual form adds the prefix chunks of
+        // the same rounds, fetched beforehand by load_prefix
+        constexpr int IT0 = RPH / (NW / 2) / RPI;   // rounds per wave, half 0 (NW/2 waves)
+        constexpr int IT1 = RPH / NW / RPI;         // rounds per wave, half 1 (all waves)
+        auto load_prefix = [&](int hh, int wi, auto NWV, auto &pv) __attribute__((always_inline)) {
             constexpr int per = RPH / decltype(NWV)::value;
             constexpr int ITER = per / RPI;
-            // the prefix chunks this lane adds (residual form), all in flight at once
-            u32x4_t pv[RES ? ITER : 1];
-            if constexpr (RES) {
 #pragma unroll
-                for (int i = 0; i < ITER; ++i) {
-                    const int r = hh * RPH + wi * per + i * RPI + l / LPR;
-                    const int j = j0 + 8 * (l % LPR);
-                    pv[i] = lt_buf_load16(rp, j + 8 <= n ? (uint32_t)(((int64_t)r * ld_pre + j) * 2)
-                                                         : LT_OOB);
-                }
+            for (int i = 0; i < ITER; ++i) {
+                const int r = hh * RPH + wi * per + i * RPI + l / LPR;
+                const int j = j0 + 8 * (l % LPR);
+                pv[i] = lt_buf_load16(rp, j + 8 <= n ? (uint32_t)(((int64_t)r * ld_pre + j) * 2)
+                                                     : LT_OOB);
             }
+        };
+        auto write_back = [&](const char *half, int hh, int wi, auto NWV, const auto &pv)
+            __attribute__((always_inline)) {
+            constexpr int per = RPH / decltype(NWV)::value;
+            constexpr int ITER = per / RPI;
 #pragma unroll
             for (int i = 0; i < ITER; ++i) {
                 const int rh = wi * per + i * RPI + l / LPR;
@@ -443,16 +449,30 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
             }
         };
         static_assert((RPH / (NW / 2)) % RPI == 0 && (RPH / NW) % RPI == 0, "whole store rounds");
-        if (h == 0) sums(st0);
-        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+        static_assert(2 * IT0 + IT1 < 63, "stores and prefix loads fit the vmcnt field");
+        // Each wave first puts the prefix chunks it adds next in flight.  Half
+        // 0 is summed by its own waves; once half 1 has landed (its loads are
+        // older than the prefix loads) the half-1 waves sum while the half-0
+        // waves write half 0 back.  The second hand-off waits for LDS only,
+        // leaving the half-0 stores in flight.
+        u32x4_t pv0[RES ? IT0 : 1], pv1[RES ? IT1 : 1];
+        if (h == 0) {
+            const int wi = wj * (WGT / 2) + wt;
+            if constexpr (RES) load_prefix(0, wi, I<NW / 2>{}, pv0);
+            sums(st0);
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? IT0 : 0));
+            lt_lds_barrier();
+            if constexpr (RES) load_prefix(1, w, I<NW>{}, pv1);
+            write_back(st0, 0, wi, I<NW / 2>{}, pv0);
+        } else {
+            if constexpr (RES) load_prefix(1, w, I<NW>{}, pv1);
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? IT1 : 0));
+            lt_lds_barrier();
+            sums(st1);
+        }
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));
         lt_lds_barrier();
-        // half 1 has landed and half 0 is summed: the half-1 waves sum while
-        // the half-0 waves write half 0 back
-        if (h == 1) sums(st1);
-        else write_back(st0, 0, wj * (WGT / 2) + wt, I<NW / 2>{});
-        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
-        lt_lds_barrier();
-        write_back(st1, 1, w, I<NW>{});
+        write_back(st1, 1, w, I<NW>{}, pv1);
     } else {
         // ---- plain epilogue (unaligned `out`): element-wise read-add-round-write
 #pragma unroll
