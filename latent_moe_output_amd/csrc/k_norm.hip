@@ -8,40 +8,61 @@
 // written once.
 //
 // One workgroup per 16-token tile, built by the same tile code (lt_latent.h)
-// as the weight-streaming kernel, so both paths give identical latents; the
-// registers are then stored to the packed [T][L] latent.
+// as the weight-streaming kernel, so both paths give identical latents.  The
+// tile moves between memory and registers through the staged LDS layout of
+// lt_latent.h, so loads and stores cover whole 128-byte lines.
 #include "lt_internal.h"
 #include "lt_latent.h"
 
 namespace lt {
 namespace {
 
-template <int NI>
+template <int NI, bool ST>
 __global__ __launch_bounds__(64 * KW) void k_sum_rmsnorm(const u16 *__restrict__ part,
                                                          int64_t pstride, int P, int64_t T, int L,
                                                          const u16 *__restrict__ norm_w, float eps,
                                                          float inv_L, u16 *__restrict__ y)
 {
     __shared__ float red[1][KW * 16];
+    __shared__ __attribute__((aligned(1024))) char lds_t[latent_stage_bytes<1, NI>()];
     const int64_t t0 = (int64_t)blockIdx.x * 16;
     const int Tv = (int)min((int64_t)16, T - t0);
     const u16 *tile = part + t0 * L;
 
+    // one partial: the tile is copied into LDS as whole lines (ST); several:
+    // loaded and summed in registers
     u32x4_t sv[1][NI], wv[NI];
-    latent_load(tile, Tv, L, sv[0]);
+    if constexpr (ST) latent_stage<1, NI>(tile, Tv, L, lds_t);
+    else latent_load(tile, Tv, L, sv[0]);
     if (norm_w) latent_load_weight(norm_w, L, wv);
-    latent_sum(tile, pstride, P, Tv, L, sv[0]);
+    if constexpr (ST) {
+        if (norm_w) __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(NI));
+        else __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+        lt_lds_barrier();
+        if (norm_w) latent_from_lds<1, NI>(lds_t, sv);
+    } else {
+        latent_sum(tile, pstride, P, Tv, L, sv[0]);
+    }
+    // the normalised tile goes back into the staged layout (each slot is
+    // written by the lane that read it) and is stored from there as whole
+    // lines; without the norm a staged tile is already there
     if (norm_w) latent_norm<1, NI>(sv, wv, eps, inv_L, red);
-
+    if (!ST || norm_w) {
+        latent_to_lds<1, NI>(lds_t, sv);
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));
+        lt_lds_barrier();
+    }
+    constexpr int SPR = 32 * NI;
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t = l & 15, g = l >> 4;
     const int nchunk = L >> 3;
-    if (t >= Tv) return;
-    u16 *row = y + (t0 + t) * L;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int c = 4 * KW * i + 4 * w + g;
-        if (c < nchunk) *reinterpret_cast<u32x4_t *>(row + c * 8) = sv[0][i];
+    for (int k = 0; k < NI; ++k) {
+        const int m = KW * k + w;
+        const int slot = 64 * m + l;
+        const int row = slot / SPR, c = (slot % SPR) ^ (row & 15);
+        if (row < Tv && c < nchunk)
+            *reinterpret_cast<u32x4_t *>(y + (t0 + row) * L + c * 8) =
+                *reinterpret_cast<const u32x4_t *>(lds_t + 16 * slot);
     }
 }
 
@@ -50,8 +71,12 @@ hipError_t launch_ni(const u16 *part, int64_t pstride, int P, int64_t T, int L,
                      const u16 *norm_w, float eps, u16 *y, hipStream_t stream)
 {
     const dim3 grid((unsigned)((T + 15) / 16)), block(64 * KW);
-    hipLaunchKernelGGL((k_sum_rmsnorm<NI>), grid, block, 0, stream, part, pstride, P, T, L,
-                       norm_w, eps, 1.0f / (float)L, y);
+    if (P == 1)
+        hipLaunchKernelGGL((k_sum_rmsnorm<NI, true>), grid, block, 0, stream, part, pstride, P, T,
+                           L, norm_w, eps, 1.0f / (float)L, y);
+    else
+        hipLaunchKernelGGL((k_sum_rmsnorm<NI, false>), grid, block, 0, stream, part, pstride, P, T,
+                           L, norm_w, eps, 1.0f / (float)L, y);
     return hipGetLastError();
 }
 

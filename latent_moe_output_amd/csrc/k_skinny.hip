@@ -15,12 +15,14 @@
 //    are loaded straight into registers in the A-operand layout of
 //    v_mfma_f32_16x16x32_bf16 (row = lane % 16, 8 consecutive k per lane), so
 //    W never passes through LDS.
-//  * The partial chunks are loaded first (and, with several partials, summed
-//    before anything else is issued, so the sum's waits never drain the W
-//    stream), then the norm weight, then all of the workgroup's W chunks,
-//    then the out values the epilogue will add to: the whole W share is in
-//    flight while the latent is normalised, and the read-modify-write of the
-//    window adds no memory round trip at the end.
+//  * The out values the epilogue will add to are fetched first, then the
+//    latent (one partial: copied into LDS as whole lines and read back in the
+//    operand layout, see lt_latent.h; several: loaded and summed in
+//    registers before anything else is issued, so the sum's waits never
+//    drain the W stream), then the norm weight, then all of the workgroup's
+//    W chunks: the whole W share is in flight while the latent is
+//    normalised, and the read-modify-write of the window adds no memory
+//    round trip at the end.
 //  * The latent is built in registers in the B-operand layout (token = lane
 //    % 16) by the shared tile code of lt_latent.h; splitting K over KW waves
 //    keeps each lane's share of the RMSNorm arithmetic small, and the norm's
@@ -40,7 +42,7 @@
 namespace lt {
 namespace {
 
-template <int NI, int TT, int JT, bool RES>
+template <int NI, int TT, int JT, bool RES, bool ST>
 __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part, int64_t pstride,
                                                     int P, int T, int L,
                                                     const u16 *__restrict__ norm_w, float eps,
@@ -59,16 +61,39 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
     const int rows = min(RW, n - j0);   // 1..RW rows of this block are in the window
 
     __shared__ float red_ss[TT][KW * 16];
-    __shared__ f32x4_t red_acc[KW][JT * TT][64];
+    // The staged latent tiles (one partial, ST) and, once the latent is in
+    // registers, the per-wave partial products share one LDS area.
+    constexpr int STAGE_BYTES = ST ? latent_stage_bytes<TT, NI>() : 0;
+    constexpr int RED_BYTES = KW * JT * TT * 64 * 16;
+    __shared__ __attribute__((aligned(1024))) char lds_u[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
+    auto red_acc = reinterpret_cast<f32x4_t (*)[JT * TT][64]>(lds_u);
 
-    // 1. partials (summed first when there are several, so that the sum's
-    //    waits cover partial loads only), then norm weight, W rows, out values
+    // this wave's epilogue fragment (w < JT*TT): token tile w % TT, row tile w / TT
+    const bool has_epi = w < JT * TT;
+    const int tte = w % TT, jte = w / TT;
+    const int te = 16 * tte + r, jl = 16 * jte + 4 * g;   // token, local row
+    const bool out_vec = has_epi && te < T && vec8 && jl + 4 <= rows;
+
+    // 1. the out values the epilogue adds to (first, so that every later wait
+    //    counts the same loads in every wave), the latent (one partial: copied
+    //    into LDS as whole lines; several: loaded and summed in registers
+    //    before anything else is issued, so the sum's waits cover partial
+    //    loads only), the norm weight, then all of this block's W rows
+    u32x2_t opre = {0u, 0u}, ppre = {0u, 0u};
+    if (out_vec) {
+        opre = *reinterpret_cast<const u32x2_t *>(outn + (int64_t)te * ld_out + j0 + jl);
+        if constexpr (RES) ppre = *reinterpret_cast<const u32x2_t *>(prefn + (int64_t)te * ld_pre + j0 + jl);
+    }
     u32x4_t sv[TT][NI];
+    if constexpr (ST) {
+        latent_stage<TT, NI>(part, T, L, lds_u);
+    } else {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) latent_load(part + (int64_t)16 * tt * L, T - 16 * tt, L, sv[tt]);
+        for (int tt = 0; tt < TT; ++tt) latent_load(part + (int64_t)16 * tt * L, T - 16 * tt, L, sv[tt]);
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-        latent_sum(part + (int64_t)16 * tt * L, pstride, P, T - 16 * tt, L, sv[tt]);
+        for (int tt = 0; tt < TT; ++tt)
+            latent_sum(part + (int64_t)16 * tt * L, pstride, P, T - 16 * tt, L, sv[tt]);
+    }
     u32x4_t wv[NI];
     if (norm_w) latent_load_weight(norm_w, L, wv);
     u32x4_t wa[JT][NI];
@@ -84,15 +109,17 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
                 wa[jt][i] = lt_buf_load16(rw, off);
             }
     }
-    // this wave's epilogue fragment (w < JT*TT): token tile w % TT, row tile w / TT
-    const bool has_epi = w < JT * TT;
-    const int tte = w % TT, jte = w / TT;
-    const int te = 16 * tte + r, jl = 16 * jte + 4 * g;   // token, local row
-    const bool out_vec = has_epi && te < T && vec8 && jl + 4 <= rows;
-    u32x2_t opre = {0u, 0u}, ppre = {0u, 0u};
-    if (out_vec) {
-        opre = *reinterpret_cast<const u32x2_t *>(outn + (int64_t)te * ld_out + j0 + jl);
-        if constexpr (RES) ppre = *reinterpret_cast<const u32x2_t *>(prefn + (int64_t)te * ld_pre + j0 + jl);
+    if constexpr (ST) {
+        // the staged tiles have landed once at most the norm-weight and W
+        // loads issued after them are in flight
+        if (norm_w) __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(NI + JT * NI));
+        else __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(JT * NI));
+        lt_lds_barrier();
+        latent_from_lds<TT, NI>(lds_u, sv);
+        if (!norm_w) {   // the products below reuse the staging area
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));
+            lt_lds_barrier();
+        }
     }
 
     // 2. RMSNorm (its barrier waits for LDS only; W stays in flight)
@@ -172,14 +199,20 @@ hipError_t launch_nt(const u16 *part, int64_t pstride, int P, int T, int L, cons
                      const Resid *res, hipStream_t stream)
 {
     const dim3 grid((n + RW - 1) / RW), block(64 * KW);
-    if (res)
-        hipLaunchKernelGGL((k_skinny<NI, TT, JT, true>), grid, block, 0, stream, part, pstride, P,
-                           T, L, norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8,
-                           res->prefix, res->ld_prefix, res->resid, res->ld_resid);
-    else
-        hipLaunchKernelGGL((k_skinny<NI, TT, JT, false>), grid, block, 0, stream, part, pstride,
-                           P, T, L, norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8,
-                           nullptr, (int64_t)0, nullptr, (int64_t)0);
+    const u16 *pre = res ? res->prefix : nullptr;
+    u16 *rsd = res ? res->resid : nullptr;
+    const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
+#define LT_SKINNY_LAUNCH(R, S)                                                                  \
+    hipLaunchKernelGGL((k_skinny<NI, TT, JT, R, S>), grid, block, 0, stream, part, pstride, P, T, \
+                       L, norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8, pre, ldp,  \
+                       rsd, ldr)
+    // one partial: the latent tiles are staged through LDS as whole lines
+    if (res) {
+        if (P == 1) LT_SKINNY_LAUNCH(true, true); else LT_SKINNY_LAUNCH(true, false);
+    } else {
+        if (P == 1) LT_SKINNY_LAUNCH(false, true); else LT_SKINNY_LAUNCH(false, false);
+    }
+#undef LT_SKINNY_LAUNCH
     return hipGetLastError();
 }
 

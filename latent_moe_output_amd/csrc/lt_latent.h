@@ -56,6 +56,81 @@ __device__ __forceinline__ void latent_load(const u16 *__restrict__ tile, int Tv
     for (int i = 0; i < NI; ++i) sv[i] = lt_buf_load16(r, latent_offset(i, L));
 }
 
+// ---- LDS staging of a partial's tiles.
+//
+// Loading the B-operand layout straight from memory makes every load
+// instruction touch 16 rows at the same 64-byte offset of each row; on this
+// chip's vector L1 that pattern moves about a third of what whole contiguous
+// lines move (about 21 vs 58 bytes per clock per CU, measured).  So the tile
+// is first copied into LDS as whole lines by direct-to-LDS loads, 1 KB of
+// contiguous row data per wave instruction, then read back in the operand
+// layout.
+//
+// Staged layout: row r (token 16*tt + t) holds 32*NI slots of 16 bytes at
+// lds + r * NI * 512; global chunk c of the row sits in slot c ^ (r & 15).
+// The XOR keeps the 16 lanes that read one chunk of 16 rows on distinct LDS
+// banks, and keeps every aligned group of 4 lanes of a copy instruction on
+// 4 consecutive chunks of one line.  Slots past the row end and rows past
+// Tv hold zeros.
+template <int TT, int NI>
+constexpr int latent_stage_bytes() { return 16 * TT * NI * 512; }
+
+// Issues the copy of tokens [0, min(Tv, 16*TT)) of partial 0 (row stride L)
+// into the staged layout: TT*NI direct loads per wave, all KW waves taking
+// part.  The caller waits for them (vmcnt) and runs a workgroup barrier
+// before latent_from_lds.
+template <int TT, int NI>
+__device__ __forceinline__ void latent_stage(const u16 *__restrict__ tile, int Tv, int L, char *lds)
+{
+    static_assert((NI & (NI - 1)) == 0, "slots per row must be a power of two");
+    constexpr int SPR = 32 * NI;                  // 16-byte slots per staged row
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t r = lt_rsrc(tile, latent_tile_bytes(Tv < 16 * TT ? Tv : 16 * TT, L));
+#pragma unroll
+    for (int k = 0; k < TT * NI; ++k) {
+        const int m = KW * k + w;                 // 1 KB block of the staging area
+        const int slot = 64 * m + l;
+        const int row = slot / SPR, c = (slot % SPR) ^ (row & 15);
+        const uint32_t off = c < (L >> 3) ? (uint32_t)(row * L + c * 8) * 2u : LT_OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void *)(lds + 1024 * m), 16, off, 0, 0, 0);
+    }
+}
+
+// Reads this lane's chunks of the staged tiles in the B-operand layout (the
+// same chunks latent_load would load).
+template <int TT, int NI>
+__device__ __forceinline__ void latent_from_lds(const char *lds, u32x4_t (&sv)[TT][NI])
+{
+    constexpr int SPR = 32 * NI;
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = l & 15, g = l >> 4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int c = 4 * KW * i + 4 * w + g;
+            sv[tt][i] = *reinterpret_cast<const u32x4_t *>(lds + ((16 * tt + t) * SPR + (c ^ t)) * 16);
+        }
+}
+
+// Writes this lane's chunks back into the staged layout (the inverse of
+// latent_from_lds; each slot has exactly one owner lane).
+template <int TT, int NI>
+__device__ __forceinline__ void latent_to_lds(char *lds, const u32x4_t (&sv)[TT][NI])
+{
+    constexpr int SPR = 32 * NI;
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = l & 15, g = l >> 4;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int c = 4 * KW * i + 4 * w + g;
+            *reinterpret_cast<u32x4_t *>(lds + ((16 * tt + t) * SPR + (c ^ t)) * 16) = sv[tt][i];
+        }
+}
+
 // Loads this lane's chunks of the norm weight (zeros past the row end).
 template <int NI>
 __device__ __forceinline__ void latent_load_weight(const u16 *__restrict__ norm_w, int L,
