@@ -112,7 +112,10 @@ def test_large_workload_sampled(name):
     (2000, 7100, 37, 7168, 2, 1024),   # 256 x 256 tiles, 2 stages (224 tiles), ragged both ways
     (1000, 7100, 5, 7120, 1, 1024),    # 128 x 128 tiles, 2 stages
     (500, 7100, 11, 7128, 3, 1024),    # 128 x 128 tiles, 4 stages
-    (300, 3000, 8, 3016, 1, 1024),     # 64 x 128 tiles, 4 waves, 4 stages
+    (300, 3000, 8, 3016, 1, 1024),     # 64 x 64 tiles, 4 waves, 4 stages
+    (130, 7168, 0, 7176, 1, 1024),     # 64 x 128 tiles, 4 waves, 4 stages
+    (130, 7168, 24, 7200, 2, 1032),    # 64 x 128 with a K tail
+    (129, 7100, 3, 7112, 1, 1096),     # 64 x 64 with a K tail, ragged T and n
     (2000, 7100, 64, 7168, 1, 1032),   # 256 x 256, LDS epilogue, K tail (L % 128 != 0)
     (1000, 7100, 32, 7136, 2, 1096),   # 128 x 128 / 2 stages with a K tail
     (500, 7100, 0, 7104, 1, 1160),     # 128 x 128 / 4 stages with a K tail
