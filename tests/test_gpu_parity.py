@@ -159,15 +159,17 @@ def test_dispatch_boundary_both_paths(T, thr, forced):
     assert_window_close(got, ref, wl.c0, wl.n, "T=%d thr=%d" % (T, thr))
 
 
-def test_paths_give_identical_latents(forced):
+@pytest.mark.parametrize("P", [1, 3])
+def test_paths_give_identical_latents(P, forced):
     """With W = I (H = L) and out = 0 the output is the latent itself; the
     weight-streaming and GEMM paths must produce the same bits, and those
-    bits must be the oracle's latent within tolerance."""
+    bits must be the oracle's latent within tolerance (one partial: both
+    kernels stage the tile through LDS; three: both sum in registers)."""
     from oracle import oracle
 
     L, T = 1024, 48
     rng = np.random.Generator(np.random.PCG64(3))
-    parts = synth.to_bf16_bits(rng.standard_normal((3, T, L)) * 0.6)
+    parts = synth.to_bf16_bits(rng.standard_normal((P, T, L)) * 0.6)
     nw = synth.to_bf16_bits(1 + 0.1 * rng.standard_normal(L))
     eye = synth.to_bf16_bits(np.eye(L))
     outs = []
@@ -175,8 +177,8 @@ def test_paths_give_identical_latents(forced):
         forced(thr)
         d = dict(partials=parts, norm_w=nw, W=eye, out=np.zeros((T, L), np.uint16))
         di = DevInputs(d)
-        wl = synth.Workload("eye", T=T, L=L, H=L, P=3, c0=0, n=L, ld_out=L)
-        say("identity latent thr=%d" % thr)
+        wl = synth.Workload("eye", T=T, L=L, H=L, P=P, c0=0, n=L, ld_out=L)
+        say("identity latent P=%d thr=%d" % (P, thr))
         binding.check(di.call(wl))
         _sync()
         outs.append(host(di.out))
@@ -189,23 +191,25 @@ def test_paths_give_identical_latents(forced):
 # exact cases: bit-exact against the oracle
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T", [5, 200])
-def test_dyadic_inputs_are_bit_exact(T):
+@pytest.mark.parametrize("T", [5, 40, 200])
+@pytest.mark.parametrize("P", [1, 2])
+def test_dyadic_inputs_are_bit_exact(T, P):
     """Norm off, small-integer latent, W in {-2..2}/16: every partial sum and
     projection is exact in fp32, so only the final rounding remains and the
-    GPU must equal the oracle bit for bit."""
+    GPU must equal the oracle bit for bit (one partial: the latent staged
+    through LDS goes straight to the projection)."""
     from oracle import oracle
 
     rng = np.random.Generator(np.random.PCG64(4))
     L, H = 1024, 640
-    A = rng.integers(-2, 3, (2, T, L)).astype(np.float64)
+    A = rng.integers(-2, 3, (P, T, L)).astype(np.float64)
     Wm = rng.integers(-2, 3, (H, L)) / 16.0
     C = rng.integers(-512, 513, (T, H)) / 8.0
     d = dict(partials=synth.to_bf16_bits(A), norm_w=None, W=synth.to_bf16_bits(Wm),
              out=synth.to_bf16_bits(C))
-    wl = synth.Workload("dyadic", T=T, L=L, H=H, P=2, c0=64, n=520, ld_out=H, norm=False)
+    wl = synth.Workload("dyadic", T=T, L=L, H=H, P=P, c0=64, n=520, ld_out=H, norm=False)
     di = DevInputs(d)
-    say("dyadic T=%d" % T)
+    say("dyadic T=%d P=%d" % (T, P))
     binding.check(di.call(wl))
     _sync()
     ref = oracle.latent_tail(d["partials"], None, 0.0, d["W"], wl.c0, wl.n, d["out"])
@@ -300,15 +304,32 @@ def test_edge_shapes(T, L, H, P, c0, n, ld):
 @pytest.mark.parametrize("T", [1, 17, 33, 64])
 @pytest.mark.parametrize("n,L", [(7168, 1024), (7100, 1024), (5000, 264), (4097, 1024),
                                  (9000, 520), (12, 1024)])
-def test_skinny_row_blocks(T, n, L, forced):
+@pytest.mark.parametrize("P", [1, 2])
+def test_skinny_row_blocks(T, n, L, P, forced):
     """Weight-streaming path over window widths whose row blocks (4..32 rows,
-    one or two MFMA tiles, a short last block) cover every epilogue case."""
+    one or two MFMA tiles, a short last block) cover every epilogue case, with
+    the latent staged through LDS (one partial) and summed in registers (two)."""
     forced(64)
-    wl = synth.Workload("rowblk", T=T, L=L, H=n + 11, P=2, c0=5, n=n, ld_out=n + 13,
+    wl = synth.Workload("rowblk", T=T, L=L, H=n + 11, P=P, c0=5, n=n, ld_out=n + 13,
                         part_std=0.6)
     assert binding.lt_path_for(T, n) == 1
     _, got, ref = _run_full(wl, seed=T * 7 + n)
     assert_window_close(got, ref, 5, n, "rowblk T=%d n=%d L=%d" % (T, n, L))
+
+
+@pytest.mark.parametrize("T", [32, 33, 64])
+@pytest.mark.parametrize("L", [1536, 2048])
+@pytest.mark.parametrize("P", [1, 2])
+def test_skinny_widest_latent_full_launches(T, L, P, forced):
+    """Latents over 1024 wide run at most 32 tokens per weight-streaming
+    launch (two 16-token tiles; staged through LDS, 128 KB, with one partial):
+    a full launch, a launch plus one token, and two full launches."""
+    forced(64)
+    wl = synth.Workload("wide", T=T, L=L, H=1100, P=P, c0=9, n=1031, ld_out=1104,
+                        part_std=0.6)
+    assert binding.lt_path_for(T, wl.n) == 1
+    _, got, ref = _run_full(wl, seed=T + L + P)
+    assert_window_close(got, ref, wl.c0, wl.n, "wide T=%d L=%d P=%d" % (T, L, P))
 
 
 def test_sentinels_outside_window_survive():
