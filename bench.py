@@ -169,7 +169,28 @@ def context_pass(binding, hip, stream, sh, sets, wpool, norm_w, reps=20):
         ctx["warm_same_buffers"] = warm
         hip.destroy(a)
         hip.destroy(b)
+    ctx["clocks"] = gpu_clocks()
     return ctx
+
+
+def gpu_clocks():
+    """The clock lines `rocm-smi --showclocks` prints for the first card
+    (current levels right after the timed work), or None where the tool is
+    missing or fails."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        cards = json.loads(r.stdout)
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+    if not isinstance(cards, dict) or not cards:
+        return None
+    first = cards[sorted(cards)[0]]
+    if not isinstance(first, dict):
+        return None
+    return {k: v for k, v in first.items() if "clock" in k.lower() or "clk" in k.lower()}
 
 
 def residual_pass(binding, hip, stream, sh, sets, wpool, norm_w, call_kern, reps=20):

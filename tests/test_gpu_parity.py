@@ -80,6 +80,16 @@ def test_decode_workload(T):
     assert_window_close(got, ref, wl.c0, wl.n, "decode T=%d" % T)
 
 
+@pytest.mark.parametrize("T,seed", [(1, 10), (5, 11), (8, 12), (16, 13), (5, 14)])
+def test_pages_token_sweep(T, seed):
+    """The token counts the pages' own equivalence test sweeps ([PR51253 Key
+    source snippets, `_check_matches_replicated`]: 1, 5, 8, 16, 5), on the
+    decode shape with a fresh seed per entry."""
+    wl = synth.WORKLOADS["decode"].with_T(T)
+    _, got, ref = _run_full(wl, seed=seed)
+    assert_window_close(got, ref, wl.c0, wl.n, "pages sweep T=%d seed=%d" % (T, seed))
+
+
 def test_shard_workload():
     wl = synth.WORKLOADS["shard"]
     _, got, ref = _run_full(wl)
