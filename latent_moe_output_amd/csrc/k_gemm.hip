@@ -181,7 +181,11 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
     // block, chunk 2*ks + l/32 of the stage row for K slice ks.
     const int hsel = l >> 5;
     const int arow = wj * (BJ / WGJ) + perm32(l & 31);
-    const int brow = wt * (BT / WGT) + perm32(l & 31);   // token of this lane's D column
+    // A wave's token rows are the 32-row blocks WGT*mt + wt of the tile (not
+    // one contiguous range), so every wave owns rows in both halves of the
+    // out tile and all waves share the work of each epilogue half.
+    constexpr int BSTR = 32 * WGT;                       // tile rows between a wave's blocks
+    const int brow = 32 * wt + perm32(l & 31);           // token of this lane's D column, block 0
     const int abase = arow * ROWB, bbase = STAGE_A + brow * ROWB;
     const int akey = swz8(arow), bkey = swz8(brow);      // perm32 keeps r % 32 -> same key per block
     auto read_frags = [&](auto S, int ks, bf16x8_t (&fa)[MJ], bf16x8_t (&fb)[MT])
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
             fa[mj] = *reinterpret_cast<const bf16x8_t *>(base + abase + mj * 32 * ROWB + ca);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            fb[mt] = *reinterpret_cast<const bf16x8_t *>(base + bbase + mt * 32 * ROWB + cb);
+            fb[mt] = *reinterpret_cast<const bf16x8_t *>(base + bbase + mt * BSTR * ROWB + cb);
     };
 
     f32x16_t acc[MJ][MT];
@@ -328,25 +332,16 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
     }
 
     if constexpr (EPI_LDS) {
-        // half 0 goes to st0 and half 1 to st1.  With two stages half 1 is
-        // fetched here, once every wave is past its last reads of st1; with
-        // more it is already in flight.
-        if constexpr (NS == 2) {
-            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
-            lt_lds_barrier();
-            load_c_half(st1, 1);
-        } else {
-            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(HLD));
-            lt_lds_barrier();
-        }
-        // sums in place for the rows this wave owns (its token half h = wt / (WGT/2))
-        const int h = wt / (WGT / 2);
+        // half 0 goes to st0 and half 1 to st1 (with two stages half 1 is
+        // fetched below, once st1 is free; with more it is already in flight)
+        // sums in place for the rows of half hh this wave owns
         const bool edge = j0 + BJ > n;            // the window ends inside this tile
-        auto sums = [&](char *half) __attribute__((always_inline)) {
+        auto sums = [&](char *half, int hh) __attribute__((always_inline)) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int r = brow + 32 * mt;             // tile row (token)
-                const int rh = r - h * RPH;               // row within the half
+                if ((BSTR * mt + 32 * wt) / RPH != hh) continue;   // block in the other half
+                const int r = brow + BSTR * mt;           // tile row (token)
+                const int rh = r - hh * RPH;              // row within the half
 #pragma unroll
                 for (int mj = 0; mj < MJ; ++mj) {
 #pragma unroll
@@ -391,8 +386,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
         // rows [wi*per, (wi+1)*per) of half hh, per = RPH / NWV, go out in
         // per / RPI store rounds; the residual form adds the prefix chunks of
         // the same rounds, fetched beforehand by load_prefix
-        constexpr int IT0 = RPH / (NW / 2) / RPI;   // rounds per wave, half 0 (NW/2 waves)
-        constexpr int IT1 = RPH / NW / RPI;         // rounds per wave, half 1 (all waves)
+        constexpr int IT = RPH / NW / RPI;          // store rounds per wave and half
         auto load_prefix = [&](int hh, int wi, auto NWV, auto &pv) __attribute__((always_inline)) {
             constexpr int per = RPH / decltype(NWV)::value;
             constexpr int ITER = per / RPI;
@@ -448,36 +442,40 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
                 }
             }
         };
-        static_assert((RPH / (NW / 2)) % RPI == 0 && (RPH / NW) % RPI == 0, "whole store rounds");
-        static_assert(2 * IT0 + IT1 < 63, "stores and prefix loads fit the vmcnt field");
-        // Each wave first puts the prefix chunks it adds next in flight.  Half
-        // 0 is summed by its own waves; once half 1 has landed (its loads are
-        // older than the prefix loads) the half-1 waves sum while the half-0
-        // waves write half 0 back.  The second hand-off waits for LDS only,
-        // leaving the half-0 stores in flight.
-        u32x4_t pv0[RES ? IT0 : 1], pv1[RES ? IT1 : 1];
-        if (h == 0) {
-            const int wi = wj * (WGT / 2) + wt;
-            if constexpr (RES) load_prefix(0, wi, I<NW / 2>{}, pv0);
-            sums(st0);
-            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? IT0 : 0));
-            lt_lds_barrier();
-            if constexpr (RES) load_prefix(1, w, I<NW>{}, pv1);
-            write_back(st0, 0, wi, I<NW / 2>{}, pv0);
-        } else {
-            if constexpr (RES) load_prefix(1, w, I<NW>{}, pv1);
-            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? IT1 : 0));
-            lt_lds_barrier();
-            sums(st1);
+        static_assert((RPH / NW) % RPI == 0, "whole store rounds");
+        static_assert(2 * IT < 63, "prefix loads fit the vmcnt field");
+        // Every wave sums its blocks of half 0, then (half 1 landed) writes
+        // half 0 back and sums its blocks of half 1, then writes half 1 back.
+        // The residual form's prefix chunks for both halves are in flight
+        // from the start; they were issued after half 0's loads, so waiting
+        // for half 0 leaves them flying.
+        u32x4_t pv0[RES ? IT : 1], pv1[RES ? IT : 1];
+        if constexpr (RES) {
+            load_prefix(0, w, I<NW>{}, pv0);
+            load_prefix(1, w, I<NW>{}, pv1);
         }
-        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));
+        if constexpr (NS == 2) {
+            // half 1 is fetched once every wave is past its last reads of st1
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? 2 * IT : 0));
+            lt_lds_barrier();
+            load_c_half(st1, 1);
+        } else {
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(HLD + (RES ? 2 * IT : 0)));
+            lt_lds_barrier();
+        }
+        sums(st0, 0);
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));   // half 1 (and the prefix chunks)
+        lt_lds_barrier();
+        write_back(st0, 0, w, I<NW>{}, pv0);
+        sums(st1, 1);
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));  // LDS only: half-0 stores may fly
         lt_lds_barrier();
         write_back(st1, 1, w, I<NW>{}, pv1);
     } else {
         // ---- plain epilogue (unaligned `out`): element-wise read-add-round-write
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int64_t t = t0 + brow + 32 * mt;
+            const int64_t t = t0 + brow + BSTR * mt;
             if (t >= T) continue;
             u16 *orow = outn + t * ld_out;
 #pragma unroll
