@@ -8,8 +8,9 @@
 //
 // Layout on gfx950:
 //  * Workgroup tile BJ (W rows = output columns) x BT (tokens), WGJ x WGT
-//    waves.  Each wave owns (BJ/WGJ) x (BT/WGT) as 32 x 32 tiles of
-//    v_mfma_f32_32x32x16_bf16 with W as the A operand and the latent as B.
+//    waves.  Each wave owns BJ/WGJ W rows and the 32-token blocks
+//    WGT*mt + wt of the tile, as 32 x 32 tiles of v_mfma_f32_32x32x16_bf16
+//    with W as the A operand and the latent as B.
 //  * K advances 64 at a time through NS (2 or 4) LDS stages filled straight
 //    from L2 by buffer_load_dwordx4 ... lds: while one stage is multiplied
 //    the next NS-1 are in flight.  A stage row is 64 bf16 = one whole
@@ -30,8 +31,9 @@
 //  * Epilogue: the `out` tile moves through LDS in two halves of token rows,
 //    fetched into stage arrays as soon as the K loop frees them (with two
 //    stages: half 0 during the last K stage, half 1 once the MFMAs are done,
-//    while the waves owning half 0 form their sums).  Sums are rounded once
-//    in place and the tile is written back row by row, so every store covers
+//    while every wave forms its sums of half 0 -- the interleaved token
+//    blocks give every wave rows in both halves).  Sums are rounded once in
+//    place and the tile is written back row by row, so every store covers
 //    whole contiguous row segments of `out`.  The residual form (RES) adds
 //    the prefix chunks to the rounded rows on the way out and stores the
 //    residual the same way ([PR50593 Key source snippets,
