@@ -66,14 +66,19 @@ struct Scratch {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
+// g_mu guards the map and every buffer in it: a caller holds it from looking
+// a buffer up until the kernels that use it are enqueued, so another thread
+// that grows (frees and reallocates) the same stream's buffer either runs
+// first or synchronises the stream after those kernels are in it.
 std::mutex g_mu;
 std::map<std::pair<int, uintptr_t>, Scratch> g_scratch;
 
+// Returns a scratch buffer of at least `bytes` for (current device, stream).
+// The caller holds g_mu.
 int ensure_scratch(size_t bytes, hipStream_t stream, void **out_ptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return LT_ERR_HIP;
-    std::lock_guard<std::mutex> lock(g_mu);
     Scratch &s = g_scratch[{dev, reinterpret_cast<uintptr_t>(stream)}];
     if (s.bytes >= bytes) {
         *out_ptr = s.ptr;
@@ -165,6 +170,7 @@ int lt_reserve(int64_t max_T, int64_t L, void *stream)
     if (!mul_ok(max_T, L, &elems) || elems > INT64_MAX / 2) return LT_ERR_INVALID_ARG;
     if (elems == 0) return LT_OK;
     void *p = nullptr;
+    std::lock_guard<std::mutex> lock(g_mu);
     return ensure_scratch((size_t)elems * 2, reinterpret_cast<hipStream_t>(stream), &p);
 }
 
@@ -273,6 +279,8 @@ int tail_impl(const void *partials, int n_partials, int64_t T, int64_t L, const 
         return record_hook(g_ev_after, s) ? LT_OK : LT_ERR_HIP;
     }
 
+    // the scratch stays locked until both kernels that use it are enqueued
+    std::lock_guard<std::mutex> lock(g_mu);
     void *scratch = nullptr;
     int st = ensure_scratch((size_t)tl * 2, s, &scratch);
     if (st != LT_OK) return st;
