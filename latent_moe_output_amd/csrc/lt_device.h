@@ -67,16 +67,6 @@ __device__ __forceinline__ float lt_inv_rms(float total, float inv_L, float eps)
     return rsqrtf(__builtin_fmaf(total, inv_L, eps));
 }
 
-// y = bf16((s * r) * w) for one chunk; w given as packed bf16.
-__device__ __forceinline__ u32x4_t lt_scale_chunk(const float s[8], float r, u32x4_t w)
-{
-    float wf[8], y[8];
-    lt_unpack8(w, wf);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (s[e] * r) * wf[e];
-    return lt_pack8(y);
-}
-
 // s_waitcnt immediate (gfx9 encoding): wait until at most `n` vector memory
 // operations are outstanding and all LDS operations have completed.
 constexpr int lt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }

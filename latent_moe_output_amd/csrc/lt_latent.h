@@ -17,7 +17,9 @@
 // The sum of squares of each token is taken on the matrix cores: with the
 // tile S in both operand slots, v_mfma_f32_16x16x32_bf16 accumulates S * S^T,
 // whose diagonal holds each token's sum of squares over the wave's chunks.
-// The KW per-wave sums are then added in wave order through LDS.
+// The KW per-wave sums are then added in wave order through LDS.  The norm
+// weight is applied on the matrix cores too (one-hot A operands, below), so
+// the vector units only multiply by each token's rsqrt and round.
 #pragma once
 
 #include "lt_device.h"
@@ -175,7 +177,34 @@ __device__ __forceinline__ void latent_sum(const u16 *__restrict__ tile, int64_t
     for (int i = 0; i < NI; ++i) sv[i] = lt_pack8(s[i]);
 }
 
-// RMSNorm of TT tiles in place: y = bf16((s * rsqrt(mean(s^2) + eps)) * w).
+// One-hot A operands that turn v_mfma_f32_16x16x32_bf16 into the norm-weight
+// scaling of one 32-wide K step: with A0/A1 in the A slot and a latent tile S
+// (B layout) in the B slot, D0[m][t] = w[k] * s[t][k] for k = 8*(m/4) + m%4
+// and D1 the same for k + 4.  Every output is one exact bf16 x bf16 product,
+// and the output layout (lane: token lane%16, rows 4*(lane/16)..+3) gives each
+// lane k = 8g..8g+3 from D0 and 8g+4..8g+7 from D1 (g = lane/16): exactly the
+// eight consecutive k its B-layout chunk holds.  Lane (m = lane%16, g) of A0
+// keeps element m%4 of its weight chunk when g == m/4, A1 element 4 + m%4.
+__device__ __forceinline__ void latent_weight_operands(const u32x4_t w, bf16x8_t &a0, bf16x8_t &a1)
+{
+    const int l = threadIdx.x & 63;
+    const int m = l & 15, g = l >> 4;
+    const bool mine = g == (m >> 2);
+    const uint32_t keep = (m & 1) ? 0xFFFF0000u : 0x0000FFFFu;
+    const int d = (m & 3) >> 1;                 // dword of element m % 4
+    u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        v0[k] = (mine && d == k) ? (w[k] & keep) : 0u;
+        v1[2 + k] = (mine && d == k) ? (w[2 + k] & keep) : 0u;
+    }
+    a0 = __builtin_bit_cast(bf16x8_t, v0);
+    a1 = __builtin_bit_cast(bf16x8_t, v1);
+}
+
+// RMSNorm of TT tiles in place: y = bf16((s * w) * rsqrt(mean(s^2) + eps)),
+// with s * w exact (one bf16 x bf16 product, formed on the matrix cores by
+// the one-hot operands above) and one fp32 rounding before the bf16 one.
 // `red` is LDS scratch of TT * KW * 16 floats.  One workgroup barrier for all
 // tiles: every thread of the workgroup must call it.
 template <int TT, int NI>
@@ -195,8 +224,12 @@ __device__ __forceinline__ void latent_norm(u32x4_t (&sv)[TT][NI], const u32x4_t
         // D[t][t] sits in lane 16*(t/4) + t, element t % 4
         if ((l >> 4) == (t >> 2)) red[tt][w * 16 + t] = d[t & 3];
     }
+    bf16x8_t a0[NI], a1[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) latent_weight_operands(wv[i], a0[i], a1[i]);
     __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));   // LDS only: loads may stay in flight
     lt_lds_barrier();
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
         float total = red[tt][t];
@@ -205,9 +238,15 @@ __device__ __forceinline__ void latent_norm(u32x4_t (&sv)[TT][NI], const u32x4_t
         const float rs = lt_inv_rms(total, inv_L, eps);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            float s[8];
-            lt_unpack8(sv[tt][i], s);
-            sv[tt][i] = lt_scale_chunk(s, rs, wv[i]);
+            const bf16x8_t s = __builtin_bit_cast(bf16x8_t, sv[tt][i]);
+            const f32x4_t p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], s, zero, 0, 0, 0);
+            const f32x4_t p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[i], s, zero, 0, 0, 0);
+            u32x4_t y;
+            y[0] = lt_pack2(p0[0] * rs, p0[1] * rs);
+            y[1] = lt_pack2(p0[2] * rs, p0[3] * rs);
+            y[2] = lt_pack2(p1[0] * rs, p1[1] * rs);
+            y[3] = lt_pack2(p1[2] * rs, p1[3] * rs);
+            sv[tt][i] = y;
         }
     }
 }
