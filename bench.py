@@ -23,7 +23,9 @@ once, each call on its own W copy and rotation set, replayed K/G times), the
 way a serving loop launches them; `value_direct_launch` is the same K steps
 launched call by call from Python.  Per-T figures come from a separate
 instrumented pass: HIP events recorded on the benchmark stream around each
-call and, through lt_set_kernel_events, around its projection kernel.  `roofline` is for the dominant kernel (k_gemm at
+call and, through lt_set_kernel_events, around its projection kernel, each
+call queued behind a short GPU spin so that host launch time stays outside
+the events.  `roofline` is for the dominant kernel (k_gemm at
 T=8192); `roofline_skinny` for the weight-streaming kernel at T <= 16;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the T=8192
 call on this host's cores.  `roofline.traffic` is the GEMM's HBM bytes per
@@ -50,6 +52,7 @@ MFMA_BF16_PEAK = 2.5e15    # flop/s, MI355X dense bf16
 T_SWEEP = [1 << i for i in range(14)]
 L, H, P, EPS = 1024, 7168, 1, 1e-6
 N_WPOOL = 48
+SPIN_CYCLES = 200_000   # GPU spin (about 0.1 ms) queued ahead of an event-timed call
 ROTATE_BYTES = 512 << 20
 
 
@@ -211,11 +214,13 @@ def residual_pass(binding, hip, stream, sh, sets, wpool, norm_w, call_kern, reps
                 p, o = sets[T][i % len(sets[T])]
                 W = wpool[(7 * i) % len(wpool)]
                 e = ev[i - 2] if i >= 2 else None
+                torch.cuda._sleep(SPIN_CYCLES)   # host enqueue time off the timed span
                 if e:
                     binding.lt_set_kernel_events(e[0], e[1])
                 binding.check(binding.lt_latent_tail_residual(
                     p, P, T, L, norm_w, EPS, W, H, 0, H, o, H, pre[i % 2], H, rsd[i % 2], H, sh))
                 binding.lt_set_kernel_events(None, None)
+                torch.cuda._sleep(SPIN_CYCLES)
                 if e:
                     hip.record(e[2], sh)
                 torch.add(pre[i % 2], o.view(torch.bfloat16), out=rsd[i % 2])
@@ -395,6 +400,11 @@ def main():
     for s in range(KI):
         for i, T in enumerate(T_SWEEP):
             e = ev[s][i]
+            # a short spin kernel ahead of each call keeps the GPU busy while
+            # the host enqueues the events and the call, so the host's launch
+            # time does not land between the events
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(SPIN_CYCLES)
             hip.record(e[0], sh)
             binding.lt_set_kernel_events(e[1], e[2])
             st = call(T, s)
@@ -454,11 +464,15 @@ def main():
         "flops_per_launch": flops_of(Tg),
     }
     # decode kernel: back-to-back launches (each on its own W copy) between two
-    # events, so the events' own cost does not land on a 6 us kernel
+    # events, so the events' own cost does not land on a 6 us kernel.  A spin
+    # kernel queued first keeps the GPU busy while the host enqueues all of
+    # them, so the host's launch rate cannot leave gaps between the kernels.
     sk = [T for T in T_SWEEP if T <= 16]
     NB = 48
     e0, e1 = hip.event(), hip.event()
     for s_ in range(2):
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(4_000_000)
         hip.record(e0, sh)
         for i in range(NB):
             binding.check(call(sk[i % len(sk)], i))
@@ -478,7 +492,8 @@ def main():
         "kernel": "k_skinny, one 16-token tile (T=1,2,4,8,16 in turn; L=1024, n=7168)",
         "avg_launch_us": round(sk_us, 3),
         "bytes_per_launch_avg": int(sk_bytes),
-        "timing": "%d back-to-back launches between two HIP events (includes the gaps "
+        "timing": "%d back-to-back launches between two HIP events, all enqueued "
+                  "behind a spin kernel before the first event (includes the GPU's gaps "
                   "between launches)" % NB,
     }
 
