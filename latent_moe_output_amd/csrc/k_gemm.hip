@@ -557,14 +557,16 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
     // Tile shape and stage count by tile count (measured on n = 7168, T = 128
     // .. 8192, random data): the biggest tile that still gives about one tile
     // per CU.  256 x 256 and 128 x 128 tiles run 8 waves (two per SIMD, which
-    // hide each other's LDS and barrier waits); below a full round of tiles,
-    // four stages in flight hide the L2 latency that two stages leave exposed.
+    // hide each other's LDS and barrier waits); up to one tile per CU, four
+    // stages in flight hide the L2 latency that two stages leave exposed;
+    // beyond that two stages (64 KB of LDS) let two 128 x 128 tiles share a
+    // CU, so up to 512 of them run in one round (T = 896: 18.5 vs 22 us).
     // Below a round of 64 x 128 tiles, 64 x 64 tiles put twice as many
     // workgroups on the W stream (T = 128: 6.3 vs 7.7 us).
     auto tiles = [&](int bj, int bt) { return (int64_t)((n + bj - 1) / bj) * ((T + bt - 1) / bt); };
     if (tiles(256, 256) >= 224)
         return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
-    if (tiles(128, 128) >= 448)
+    if (tiles(128, 128) > 256)
         return launch_cfg<128, 128, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     if (tiles(128, 128) >= 224)
         return launch_cfg<128, 128, 4, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);

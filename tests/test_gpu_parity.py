@@ -129,7 +129,8 @@ def test_large_workload_sampled(name):
     (2000, 7100, 64, 7168, 1, 1032),   # 256 x 256, LDS epilogue, K tail (L % 128 != 0)
     (1000, 7100, 32, 7136, 2, 1096),   # 128 x 128 / 2 stages with a K tail
     (500, 7100, 0, 7104, 1, 1160),     # 128 x 128 / 4 stages with a K tail
-    (1500, 4000, 0, 4008, 1, 2048),    # widest latent, 128 x 128 / 4 stages
+    (1500, 4000, 0, 4008, 1, 2048),    # widest latent, 128 x 128 / 2 stages (384 tiles)
+    (900, 7100, 6, 7112, 2, 1024),     # 128 x 128 / 2 stages, 2 tiles per CU (392 tiles)
 ])
 def test_gemm_tile_shapes_sampled(T, n, c0, ld, P, L):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
