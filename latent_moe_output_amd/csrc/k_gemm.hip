@@ -568,7 +568,9 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
         return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     if (tiles(128, 128) > 256)
         return launch_cfg<128, 128, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
-    if (tiles(128, 128) >= 224)
+    // four-stage 128 x 128 also when 64 x 128 tiles would need a second round
+    // (T = 320: 9.9 vs 13.7 us)
+    if (tiles(128, 128) >= 224 || tiles(64, 128) > 256)
         return launch_cfg<128, 128, 4, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     if (tiles(64, 128) >= 224)
         return launch_cfg<64, 128, 2, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);

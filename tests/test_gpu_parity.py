@@ -131,6 +131,7 @@ def test_large_workload_sampled(name):
     (500, 7100, 0, 7104, 1, 1160),     # 128 x 128 / 4 stages with a K tail
     (1500, 4000, 0, 4008, 1, 2048),    # widest latent, 128 x 128 / 2 stages (384 tiles)
     (900, 7100, 6, 7112, 2, 1024),     # 128 x 128 / 2 stages, 2 tiles per CU (392 tiles)
+    (320, 7100, 5, 7112, 1, 1032),     # 128 x 128 / 4 stages where 64 x 128 needs 2 rounds
 ])
 def test_gemm_tile_shapes_sampled(T, n, c0, ld, P, L):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
