@@ -179,9 +179,12 @@ def context_pass(binding, hip, stream, sh, sets, wpool, norm_w, reps=20):
 def gpu_clocks():
     """The clock lines `rocm-smi --showclocks` prints for the first card
     (current levels right after the timed work), or None where the tool is
-    missing or fails."""
+    missing or fails, and under a profiler: its preloaded library would start
+    the GPU in the child before rocm-smi's launcher hands over to python."""
     import subprocess
 
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
                            text=True, timeout=20)
