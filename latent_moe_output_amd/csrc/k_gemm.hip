@@ -43,6 +43,10 @@
 //  * Tiles are spread so that each of the 8 XCDs receives a contiguous range
 //    of the (grouped) tile order, keeping W and latent blocks that are reused
 //    by neighbouring tiles in the same XCD's L2.
+//  * The largest tiles (256 x 256) run k_gemm_ring, the same GEMM with the
+//    operand stream on a ring of five 32 KB slots (half a K stage each), so
+//    that 96 KB of operands are in flight instead of 64 KB; its `out` tile
+//    moves in quarters through the slots.
 // Each output element's accumulation order depends on L only (K ascending in
 // 16-wide MFMA slices), not on c0, n or the tile shape.
 #include <type_traits>
@@ -505,6 +509,416 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
     }
 }
 
+// Square tiles (BJ = BT) with the operand stream on a ring of five LDS slots.
+// A K stage is two half-stages of BJ x 64 bf16 (32 KB at BJ = 256): A (W
+// rows) and B (tokens).  Half-stage h (stage h / 2) lives in slot h % 5, so
+// while stage k is multiplied out of two slots the other three hold stage
+// k + 1 and A of stage k + 2: 96 KB of operands in flight per workgroup
+// against the 64 KB of two whole 64 KB stages, in the same 160 KB of LDS.
+// Each stage fetches B of stage k + 1 and A of stage k + 2 into the slots
+// stage k - 1 left.  The `out` tile moves through four slots in quarters of
+// BT / 4 token rows: quarter 0 is fetched during stage nk - 2 (in place of A
+// of stage nk), quarters 1 and 2 during the last stage and quarter 3 once it
+// is done.  NKR = nk % 5 fixes, at compile time, the slot every stage and
+// quarter uses.  Same tile order, swizzles, K order and epilogue arithmetic
+// as k_gemm, so the results are bit-identical to it.
+template <int BJ, int WGJ, int WGT, int GROUP_J, int NKR, bool KTAIL, bool RES>
+__global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int64_t T, int L,
+                                                              const u16 *__restrict__ Wn, int n,
+                                                              u16 *__restrict__ outn, int64_t ld_out,
+                                                              int ntj, int ntt, const u16 *prefn,
+                                                              int64_t ld_pre, u16 *resn, int64_t ld_res)
+{
+    constexpr int BT = BJ;
+    constexpr int NW = WGJ * WGT;
+    constexpr int NT = 64 * NW;
+    constexpr int MJ = BJ / WGJ / 32, MT = BT / WGT / 32;
+    constexpr int LR = 8 * NW;
+    constexpr int LA = BJ / LR;                 // direct loads per thread per operand half-stage
+    constexpr int SLOT = BJ * ROWB;             // one operand's share of a K stage
+    constexpr int NFR = MJ + MT, NMF = MJ * MT;
+    static_assert(MJ >= 1 && MT == 4 && LA * LR == BJ, "tile shape");
+    __shared__ __attribute__((aligned(1024))) char sl0[SLOT];
+    __shared__ __attribute__((aligned(1024))) char sl1[SLOT];
+    __shared__ __attribute__((aligned(1024))) char sl2[SLOT];
+    __shared__ __attribute__((aligned(1024))) char sl3[SLOT];
+    __shared__ __attribute__((aligned(1024))) char sl4[SLOT];
+    auto slot = [&](auto S) __attribute__((always_inline)) -> char * {
+        constexpr int s = decltype(S)::value;
+        if constexpr (s == 0) return sl0;
+        else if constexpr (s == 1) return sl1;
+        else if constexpr (s == 2) return sl2;
+        else if constexpr (s == 3) return sl3;
+        else return sl4;
+    };
+
+    // ---- tile coordinates, buffer resources and fragment rows as in k_gemm
+    const int G = ntj * ntt;
+    const int b = blockIdx.x;
+    const int xcd = b % NUM_XCD, idx = b / NUM_XCD;
+    const int q8 = G / NUM_XCD, r8 = G % NUM_XCD;
+    const int nb = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+    const int gsize = GROUP_J * ntt;
+    const int gid = nb / gsize;
+    const int first_j = gid * GROUP_J;
+    const int gj = min(ntj - first_j, GROUP_J);
+    const int within = nb - gid * gsize;
+    const int tj = first_j + within % gj;
+    const int tt = within / gj;
+    const int j0 = tj * BJ;
+    const int64_t t0 = (int64_t)tt * BT;
+
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wj = w / WGT, wt = w % WGT;
+    const int nchunk = L >> 3;
+    const int nk = (L + BK - 1) / BK;           // K stages, no padding (at least 3)
+    const uint32_t row_bytes = (uint32_t)L * 2u;
+
+    const int rows_a = min(BJ, n - j0);
+    const int rows_b = (int)min((int64_t)BT, T - t0);
+    const __amdgpu_buffer_rsrc_t ra = lt_rsrc(Wn + (int64_t)j0 * L, (uint32_t)rows_a * row_bytes);
+    const __amdgpu_buffer_rsrc_t rb = lt_rsrc(Y + t0 * L, (uint32_t)rows_b * row_bytes);
+
+    // direct loads as in k_gemm (both operands have BJ rows, so they share
+    // the offsets); the K offset goes in the scalar offset, which keeps the
+    // unrolled stages from holding one address register per stage
+    const int lrow = 8 * w + (l >> 3);
+    const int lslot = l & 7;
+    uint32_t off[LA];
+    int ch[LA];
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+        const int row = LR * q + lrow;
+        ch[q] = lslot ^ swz8(row);
+        off[q] = (uint32_t)row * row_bytes + (uint32_t)ch[q] * 16u;
+    }
+    auto issue = [&](const __amdgpu_buffer_rsrc_t &rs, auto S, int s) __attribute__((always_inline)) {
+        char *dst = slot(S);
+        const uint32_t kbyte = (uint32_t)s * ROWB;
+#pragma unroll
+        for (int q = 0; q < LA; ++q) {
+            uint32_t vo = off[q];
+            if (KTAIL && s * CPR + ch[q] >= nchunk) vo = OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (LR * q + 8 * w) * ROWB),
+                                                     16, vo, (int)kbyte, 0, 0);
+        }
+    };
+    auto issueA = [&](auto S, int s) __attribute__((always_inline)) { issue(ra, S, s); };
+    auto issueB = [&](auto S, int s) __attribute__((always_inline)) { issue(rb, S, s); };
+
+    const int hsel = l >> 5;
+    const int arow = wj * (BJ / WGJ) + perm32(l & 31);
+    constexpr int BSTR = 32 * WGT;
+    const int brow = 32 * wt + perm32(l & 31);
+    const int abase = arow * ROWB, bbase = brow * ROWB;
+    const int akey = swz8(arow), bkey = swz8(brow);
+    // slice ks of a row sits at chunk (2 ks + hsel) ^ key = (hsel ^ key) ^ 2 ks,
+    // so its byte offset is the slice-0 offset XOR 32 ks (rows are 128-byte
+    // aligned).  The per-lane offsets pass through an empty asm at every use,
+    // so the compiler recomputes the few address operations instead of
+    // keeping one register per slot and slice alive across the loop.
+    const int xa0 = abase + ((hsel ^ akey) << 4), xb0 = bbase + ((hsel ^ bkey) << 4);
+    auto read_frags = [&](auto SA, auto SB, int ks, bf16x8_t (&fa)[MJ], bf16x8_t (&fb)[MT])
+        __attribute__((always_inline)) {
+        int xa = xa0, xb = xb0;
+        asm volatile("" : "+v"(xa), "+v"(xb));
+        const char *ba = slot(SA) + (xa ^ (32 * ks));
+        const char *bb = slot(SB) + (xb ^ (32 * ks));
+#pragma unroll
+        for (int mj = 0; mj < MJ; ++mj)
+            fa[mj] = *reinterpret_cast<const bf16x8_t *>(ba + mj * 32 * ROWB);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            fb[mt] = *reinterpret_cast<const bf16x8_t *>(bb + mt * BSTR * ROWB);
+    };
+
+    f32x16_t acc[MJ][MT];
+#pragma unroll
+    for (int mj = 0; mj < MJ; ++mj)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mj][mt] = f32x16_t{};
+    auto mfma_range = [&](const bf16x8_t (&fa)[MJ], const bf16x8_t (&fb)[MT], int lo, int hi)
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+            if (i >= lo && i < hi) {
+                const int mj = i / MT, mt = i % MT;
+                acc[mj][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mj], fb[mt], acc[mj][mt],
+                                                                      0, 0, 0);
+            }
+        }
+    };
+
+    // out tile in quarters of BT/4 token rows, one slot each
+    constexpr int CPRE = BJ / 8;
+    constexpr int RPQ = BT / 4;
+    constexpr int QCH = RPQ * CPRE;
+    constexpr int QLD = QCH / NT;
+    static_assert(QCH % NT == 0 && RPQ * BJ * 2 <= SLOT, "quarter fits a slot");
+    const __amdgpu_buffer_rsrc_t rc = lt_rsrc(
+        outn + t0 * ld_out, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_out + n) * 2));
+    auto load_c_q = [&](char *dst, int q) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < QLD; ++it) {
+            const int idx0 = it * NT + 64 * w;
+            const int idx = idx0 + l;
+            const int r = q * RPQ + idx / CPRE;
+            const int c = (idx % CPRE) ^ (r & (CPRE - 1));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rc, (lds_void *)(dst + idx0 * 16), 16,
+                (uint32_t)(((int64_t)r * ld_out + j0 + 8 * c) * 2), 0, 0, 0);
+        }
+    };
+
+    bf16x8_t fa[2][MJ], fb[2][MT];
+    auto interleave = [&](auto ND, auto NM) __attribute__((always_inline)) {
+        constexpr int nd = decltype(ND)::value, nm = decltype(NM)::value;
+        constexpr int np = nd < nm ? nd : nm;
+#pragma unroll
+        for (int i = 0; i < np; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        if constexpr (nm > np) __builtin_amdgcn_sched_group_barrier(0x008, nm - np, 0);
+        if constexpr (nd > np) __builtin_amdgcn_sched_group_barrier(0x100, nd - np, 0);
+    };
+    // K stage k at ring phase P = k % 5: operand A in slot 2P, B in 2P+1 (mod 5).
+    // MODE 0: fetch B of stage k+1 and A of stage k+2 into the slots stage k-1
+    // freed; 1 (stage nk-2): B of the last stage and out quarter 0; 2 (last):
+    // out quarters 1 and 2.
+    auto kst = [&](auto P, auto MODE, int k) __attribute__((always_inline)) {
+        constexpr int p = decltype(P)::value, mode = decltype(MODE)::value;
+        using SA = I<(2 * p) % 5>;
+        using SB = I<(2 * p + 1) % 5>;
+        using NA = I<(2 * p + 2) % 5>;
+        using NB = I<(2 * p + 3) % 5>;
+        using FA = I<(2 * p + 4) % 5>;
+        if constexpr (mode == 0) {
+            issueB(NB{}, k + 1);
+            issueA(FA{}, k + 2);
+        } else if constexpr (mode == 1) {
+            issueB(NB{}, k + 1);
+            load_c_q(slot(FA{}), 0);
+        } else {
+            load_c_q(slot(NB{}), 1);
+            load_c_q(slot(FA{}), 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KSL - 1; ++ks) {
+            read_frags(SA{}, SB{}, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            mfma_range(fa[ks & 1], fb[ks & 1], 0, NMF);
+            interleave(I<NFR>{}, I<NMF>{});
+        }
+        constexpr int KL = (KSL - 1) & 1;
+        constexpr int HALF = NMF / 2;
+        mfma_range(fa[KL], fb[KL], 0, HALF);
+        if constexpr (mode != 2) {
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(mode == 0 ? LA : QLD));
+            lt_lds_barrier();
+            read_frags(NA{}, NB{}, 0, fa[0], fb[0]);
+        }
+        mfma_range(fa[KL], fb[KL], HALF, NMF);
+        if constexpr (mode != 2) interleave(I<NFR>{}, I<NMF - HALF>{});
+    };
+
+    issueA(I<0>{}, 0);
+    issueB(I<1>{}, 0);
+    issueA(I<2>{}, 1);
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(LA));
+    lt_lds_barrier();
+    read_frags(I<0>{}, I<1>{}, 0, fa[0], fb[0]);
+
+    constexpr int RN = (NKR + 3) % 5;           // (nk - 2) % 5 normal stages after the full trips
+    int k = 0;
+    for (; k + 5 <= nk - 2; k += 5) {
+        kst(I<0>{}, I<0>{}, k);
+        kst(I<1>{}, I<0>{}, k + 1);
+        kst(I<2>{}, I<0>{}, k + 2);
+        kst(I<3>{}, I<0>{}, k + 3);
+        kst(I<4>{}, I<0>{}, k + 4);
+    }
+    if constexpr (RN > 0) kst(I<0>{}, I<0>{}, k);
+    if constexpr (RN > 1) kst(I<1>{}, I<0>{}, k + 1);
+    if constexpr (RN > 2) kst(I<2>{}, I<0>{}, k + 2);
+    if constexpr (RN > 3) kst(I<3>{}, I<0>{}, k + 3);
+    kst(I<RN>{}, I<1>{}, k + RN);
+    kst(I<(RN + 1) % 5>{}, I<2>{}, k + RN + 1);
+    constexpr int PL = (RN + 1) % 5;            // phase of the last stage
+    using Q0 = I<(2 * PL + 2) % 5>;
+    using Q1 = I<(2 * PL + 3) % 5>;
+    using Q2 = I<(2 * PL + 4) % 5>;
+    using Q3 = I<(2 * PL) % 5>;
+
+    const bool edge = j0 + BJ > n;
+    auto sums = [&](char *qb, int qq) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if ((BSTR * mt + 32 * wt) / RPQ != qq) continue;
+            const int r = brow + BSTR * mt;
+            const int rh = r - qq * RPQ;
+#pragma unroll
+            for (int mj = 0; mj < MJ; ++mj) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int c = (wj * (BJ / WGJ) + 32 * mj + 16 * hf + 8 * hsel) >> 3;
+                    const f32x16_t &a = acc[mj][mt];
+                    u32x4_t *ptr = reinterpret_cast<u32x4_t *>(
+                        qb + rh * (BJ * 2) + ((c ^ (r & (CPRE - 1))) << 4));
+                    u32x4_t ov = *ptr;
+                    const int jc = j0 + 8 * c;
+                    if (edge && jc < n && jc + 8 > n && t0 + r < T) {
+                        const u16 *src = outn + (t0 + r) * ld_out + jc;
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2) {
+                            const uint32_t lo = (jc + e < n) ? src[e] : 0u;
+                            const uint32_t hi = (jc + e + 1 < n) ? src[e + 1] : 0u;
+                            ov[e >> 1] = lo | (hi << 16);
+                        }
+                    }
+                    u32x4_t nv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        nv[e] = lt_pack2(lt_bf_lo(ov[e]) + a[8 * hf + 2 * e],
+                                         lt_bf_hi(ov[e]) + a[8 * hf + 2 * e + 1]);
+                    *ptr = nv;
+                }
+            }
+        }
+    };
+    constexpr int LPR = CPRE;
+    constexpr int RPI = 64 / LPR;
+    constexpr int ITQ = RPQ / NW / RPI;          // store rounds per wave and quarter
+    static_assert((RPQ / NW) % RPI == 0, "whole store rounds");
+    const __amdgpu_buffer_rsrc_t rp = lt_rsrc(
+        prefn + t0 * ld_pre, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_pre + n) * 2));
+    const __amdgpu_buffer_rsrc_t rr = lt_rsrc(
+        resn + t0 * ld_res, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_res + n) * 2));
+    auto load_prefix = [&](int qq, u32x4_t (&pv)[ITQ]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < ITQ; ++i) {
+            const int r = qq * RPQ + w * (RPQ / NW) + i * RPI + l / LPR;
+            const int j = j0 + 8 * (l % LPR);
+            pv[i] = lt_buf_load16(rp, j + 8 <= n ? (uint32_t)(((int64_t)r * ld_pre + j) * 2)
+                                                 : LT_OOB);
+        }
+    };
+    auto write_back = [&](const char *qb, int qq, const u32x4_t (&pv)[ITQ])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < ITQ; ++i) {
+            const int rh = w * (RPQ / NW) + i * RPI + l / LPR;
+            const int r = qq * RPQ + rh;
+            const int c = l % LPR;
+            const int64_t t = t0 + r;
+            const int j = j0 + 8 * c;
+            if (t < T && j < n) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+                    qb + rh * (BJ * 2) + ((c ^ (r & (CPRE - 1))) << 4));
+                if (j + 8 <= n) {
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        v, rc, (uint32_t)(((int64_t)r * ld_out + j) * 2), 0, 0);
+                    if constexpr (RES) {
+                        u32x4_t rv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            rv[e] = lt_pack2(lt_bf_lo(pv[i][e]) + lt_bf_lo(v[e]),
+                                             lt_bf_hi(pv[i][e]) + lt_bf_hi(v[e]));
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            rv, rr, (uint32_t)(((int64_t)r * ld_res + j) * 2), 0, 0);
+                    }
+                } else {
+                    u16 *o = outn + t * ld_out + j;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (j + e < n) {
+                            const u16 onew = (u16)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                            o[e] = onew;
+                            if constexpr (RES) {
+                                const float rs = lt_bf_lo((uint32_t)prefn[t * ld_pre + j + e]) +
+                                                 lt_bf_lo((uint32_t)onew);
+                                resn[t * ld_res + j + e] = (u16)(lt_pack2(rs, 0.f) & 0xFFFFu);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    };
+    // In flight now (in issue order): quarters 0, 1, 2.  Then the prefix
+    // chunks of all quarters (residual form), then quarter 3 once every wave
+    // is past its last reads of the last stage's slots.  Waits that come after
+    // stores count them too (stores retire in order with loads), which is
+    // exact only where every row and column of the tile is stored: other
+    // tiles wait for everything.
+    constexpr int PF = RES ? 4 * ITQ : 0;
+    constexpr int SQ = RES ? 2 * ITQ : ITQ;      // stores per wave and quarter
+    const bool interior = t0 + BT <= T && j0 + BJ <= n;
+    u32x4_t pv0[ITQ], pv1[ITQ], pv2[ITQ], pv3[ITQ];
+    if constexpr (RES) {
+        load_prefix(0, pv0);
+        load_prefix(1, pv1);
+        load_prefix(2, pv2);
+        load_prefix(3, pv3);
+    }
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(2 * QLD + PF));     // quarter 0
+    lt_lds_barrier();
+    load_c_q(slot(Q3{}), 3);
+    sums(slot(Q0{}), 0);
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? 3 * ITQ + QLD : 2 * QLD));   // quarter 1 (+ prefix 0)
+    lt_lds_barrier();
+    write_back(slot(Q0{}), 0, pv0);
+    sums(slot(Q1{}), 1);
+    if (interior) __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? 2 * ITQ + QLD + SQ : QLD + SQ));
+    else __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));         // quarter 2 (+ prefix 1)
+    lt_lds_barrier();
+    write_back(slot(Q1{}), 1, pv1);
+    sums(slot(Q2{}), 2);
+    if (interior) __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(2 * SQ));
+    else __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));         // quarter 3 (+ all prefix)
+    lt_lds_barrier();
+    write_back(slot(Q2{}), 2, pv2);
+    sums(slot(Q3{}), 3);
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));
+    lt_lds_barrier();
+    write_back(slot(Q3{}), 3, pv3);
+}
+
+template <int BJ, int WGJ, int WGT, int GROUP_J>
+hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 *outn,
+                       int64_t ld_out, const Resid *res, hipStream_t stream)
+{
+    const int ntj = (n + BJ - 1) / BJ;
+    const int64_t ntt = (T + BJ - 1) / BJ;
+    const int nk = (L + BK - 1) / BK;
+    if (nk < 3) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(ntj * ntt)), block(64 * WGJ * WGT);
+    const u16 *pre = res ? res->prefix : nullptr;
+    u16 *rsd = res ? res->resid : nullptr;
+    const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
+    const bool kt = L % BK != 0;
+#define LT_RING(NKR, KT, R)                                                                  \
+    hipLaunchKernelGGL((k_gemm_ring<BJ, WGJ, WGT, GROUP_J, NKR, KT, R>), grid, block, 0, stream, \
+                       y, T, L, Wn, n, outn, ld_out, ntj, (int)ntt, pre, ldp, rsd, ldr)
+#define LT_RING_K(NKR)                                                                       \
+    do {                                                                                     \
+        if (kt) { if (res) LT_RING(NKR, true, true); else LT_RING(NKR, true, false); }       \
+        else { if (res) LT_RING(NKR, false, true); else LT_RING(NKR, false, false); }        \
+    } while (0)
+    switch (nk % 5) {
+    case 0: LT_RING_K(0); break;
+    case 1: LT_RING_K(1); break;
+    case 2: LT_RING_K(2); break;
+    case 3: LT_RING_K(3); break;
+    default: LT_RING_K(4); break;
+    }
+#undef LT_RING_K
+#undef LT_RING
+    return hipGetLastError();
+}
+
 template <int BJ, int BT, int WGJ, int WGT, int NS, int GROUP_J>
 hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 *outn,
                       int64_t ld_out, const Resid *res, bool vec16, hipStream_t stream)
@@ -564,8 +978,15 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
     // Below a round of 64 x 128 tiles, 64 x 64 tiles put twice as many
     // workgroups on the W stream (T = 128: 6.3 vs 7.7 us).
     auto tiles = [&](int bj, int bt) { return (int64_t)((n + bj - 1) / bj) * ((T + bt - 1) / bt); };
-    if (tiles(256, 256) >= 224)
+    if (tiles(256, 256) >= 224) {
+        // the slot ring needs at least three K stages and the LDS epilogue's
+        // alignment and 32-bit tile offsets (T = 8192: 130 vs 136 us)
+        auto small = [&](int64_t ld) { return (int64_t)256 * ld * 2 < ((int64_t)1 << 31); };
+        if (L > 2 * BK && vec16 && small(ld_out) &&
+            (!res || (small(res->ld_prefix) && small(res->ld_resid))))
+            return launch_ring<256, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, stream);
         return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
+    }
     if (tiles(128, 128) > 256)
         return launch_cfg<128, 128, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     // four-stage 128 x 128 also when 64 x 128 tiles would need a second round

@@ -132,6 +132,15 @@ def test_large_workload_sampled(name):
     (1500, 4000, 0, 4008, 1, 2048),    # widest latent, 128 x 128 / 2 stages (384 tiles)
     (900, 7100, 6, 7112, 2, 1024),     # 128 x 128 / 2 stages, 2 tiles per CU (392 tiles)
     (320, 7100, 5, 7112, 1, 1032),     # 128 x 128 / 4 stages where 64 x 128 needs 2 rounds
+    # 256 x 256 on the five-slot ring: every phase of the last K stage
+    # (K stages mod 5 = 0..4), the shortest ring (3 stages) and the two-stage
+    # kernel below it (2 stages)
+    (2000, 7100, 0, 7104, 1, 1240),    # 20 K stages
+    (2000, 7100, 8, 7112, 2, 1096),    # 18
+    (2000, 7100, 16, 7120, 1, 1160),   # 19
+    (2048, 7168, 0, 7176, 1, 1024),    # 16, interior tiles only
+    (2000, 7100, 0, 7104, 1, 192),     # 3
+    (2000, 7100, 0, 7104, 1, 128),     # 2: two-stage kernel
 ])
 def test_gemm_tile_shapes_sampled(T, n, c0, ld, P, L):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an

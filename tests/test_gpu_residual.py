@@ -76,6 +76,7 @@ CASES = [
     (129, 1024, 520, 1, 3, 517, 523, 525, 527, -1),        # GEMM, element-wise epilogue
     (64, 1024, 1536, 2, 64, 1024, 1544, 1552, 1560, 0),    # forced GEMM at a skinny size
     (100, 1024, 1536, 2, 64, 1024, 1544, 1552, 1560, 1000),  # forced skinny, two launches
+    (2000, 1032, 7110, 1, 8, 7100, 7112, 7120, 7128, -1),  # 256 x 256 slot ring, K tail, ragged
 ]
 
 
