@@ -25,7 +25,7 @@ launched call by call from Python.  Per-T figures come from a separate
 instrumented pass: HIP events recorded on the benchmark stream around each
 call and, through lt_set_kernel_events, around its projection kernel, each
 call queued behind a short GPU spin so that host launch time stays outside
-the events.  `roofline` is for the dominant kernel (k_gemm at
+the events.  `roofline` is for the dominant kernel (k_gemm_ring at
 T=8192); `roofline_skinny` for the weight-streaming kernel at T <= 16;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the T=8192
 call on this host's cores.  `roofline.traffic` is the GEMM's HBM bytes per
@@ -462,7 +462,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(g_ach / MFMA_BF16_PEAK, 4),
         "traffic": gemm_traffic_bytes(),
-        "kernel": "k_gemm, 256x256 tiles, 8 waves (T=8192, L=1024, n=7168)",
+        "kernel": "k_gemm_ring, 256x256 tiles, 8 waves (T=8192, L=1024, n=7168)",
         "avg_launch_us": round(kern_us[Tg], 3),
         "flops_per_launch": flops_of(Tg),
     }
