@@ -25,7 +25,9 @@ launched call by call from Python.  Per-T figures come from a separate
 instrumented pass: HIP events recorded on the benchmark stream around each
 call and, through lt_set_kernel_events, around its projection kernel, each
 call queued behind a short GPU spin so that host launch time stays outside
-the events.  `roofline` is for the dominant kernel (k_gemm_ring at
+the events; `graph_call_us` is each T on its own: its rotation sets captured
+into one graph (each call on its own W copy) and replayed, elapsed time per
+call.  `roofline` is for the dominant kernel (k_gemm_ring at
 T=8192); `roofline_skinny` for the weight-streaming kernel at T <= 16;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the T=8192
 call on this host's cores.  `roofline.traffic` is the GEMM's HBM bytes per
@@ -418,6 +420,31 @@ def main():
     torch.cuda.synchronize()
     del graph
 
+    # ---- per-T back-to-back time: for each T its R rotation sets (each call
+    # on its own W copy) captured into one graph, replayed; per-call time =
+    # elapsed / (replays x R), gaps between launches included
+    graph_us = {}
+    for T in T_SWEEP:
+        R = len(sets[T])
+        gT = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gT, stream=stream):
+            for s in range(R):
+                binding.check(call(T, s))
+        reps = max(3, min(20, int(4000 / R / max(1.0, T / 256))))
+        with torch.cuda.stream(stream):
+            gT.replay()                                  # untimed
+            a, b = hip.event(), hip.event()
+            hip.record(a, sh)
+            for _ in range(reps):
+                gT.replay()
+            hip.record(b, sh)
+        torch.cuda.synchronize()
+        graph_us[T] = hip.elapsed_ms(a, b) * 1e3 / (reps * R)
+        hip.destroy(a)
+        hip.destroy(b)
+        del gT
+
     per_T = []
     call_us = {}
     kern_us = {}
@@ -440,6 +467,8 @@ def main():
             "roofline_us": round(roof_us, 3),
             "bound": "hbm" if b / HBM_PEAK > f / MFMA_BF16_PEAK else "mfma",
             "frac_of_roofline": round(roof_us / call_us[T], 3),
+            "graph_call_us": round(graph_us[T], 3),
+            "graph_frac_of_roofline": round(roof_us / graph_us[T], 3),
         })
     for row in ev:
         for e4 in row:
