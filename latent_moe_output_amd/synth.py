@@ -105,3 +105,24 @@ def generate(wl: Workload, seed: int = 0) -> dict:
         out_f = np.where(mask, sign * wl.outlier_value, out_f)
     out = to_bf16_bits(out_f)
     return dict(partials=partials, norm_w=norm_w if wl.norm else None, W=W, out=out)
+
+
+def generate_device(wl: Workload, seed: int = 0, device="cuda") -> dict:
+    """The same distributions as generate(), drawn on the device by torch's
+    seeded generator, for shapes too large to draw on the host.  Every entry
+    is an int16 tensor of bf16 bit patterns (fp32 draws rounded to bf16, so
+    not bit-identical to generate()); outliers are not drawn."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape, std, mean=0.0):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        return (x * std + mean).to(torch.bfloat16).view(torch.int16)
+
+    partials = draw((wl.P, wl.T, wl.L), wl.part_std)
+    norm_w = draw((wl.L,), 0.1, 1.0)
+    W = draw((wl.H, wl.L), wl.w_std)
+    out = draw((wl.T, wl.ld_out), wl.out_std)
+    return dict(partials=partials, norm_w=norm_w if wl.norm else None, W=W, out=out)
