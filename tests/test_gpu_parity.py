@@ -281,10 +281,17 @@ def test_shards_concatenate_bit_exact(T):
     np.testing.assert_array_equal(host(part.out), host(full.out))
 
 
-@pytest.mark.parametrize("T", [7, 130])
-def test_split_partials_bit_exact(T):
-    """[X, Y, -Y] and [X/2, X/2] give the same bits as [X]."""
-    wl = synth.Workload("split", T=T, L=1024, H=512, P=1, c0=0, n=512, ld_out=512)
+@pytest.mark.parametrize("T,H,norm", [(7, 512, True), (130, 512, True), (130, 512, False),
+                                      (1000, 1024, False), (2048, 7168, False),
+                                      (2048, 7168, True)])
+def test_split_partials_bit_exact(T, H, norm):
+    """[X, Y, -Y] and [X/2, X/2] give the same bits as [X].  With the norm off
+    the large-token path multiplies one partial in place and sums several
+    first, so this also ties the two routes together; the one-partial result
+    is checked against the oracle on sampled rows."""
+    from oracle import oracle
+
+    wl = synth.Workload("split", T=T, L=1024, H=H, P=1, c0=0, n=H, ld_out=H, norm=norm)
     d = synth.generate(wl, seed=7)
     X = d["partials"]
     Y = synth.generate(wl, seed=8)["partials"]
@@ -293,12 +300,15 @@ def test_split_partials_bit_exact(T):
     for parts in (X, np.concatenate([X, Y, Y ^ 0x8000]), np.concatenate([half, half])):
         dd = dict(d, partials=parts)
         di = DevInputs(dd)
-        say("split partials T=%d P=%d" % (T, parts.shape[0]))
+        say("split partials T=%d H=%d norm=%s P=%d" % (T, H, norm, parts.shape[0]))
         binding.check(di.call(wl))
         _sync()
         results.append(host(di.out))
     np.testing.assert_array_equal(results[1], results[0])
     np.testing.assert_array_equal(results[2], results[0])
+    rows = sorted({0, T // 2, T - 1})
+    ref = oracle.latent_tail(X[:, rows, :], d["norm_w"], eps32(wl), d["W"], 0, H, d["out"][rows])
+    assert_window_close(results[0][rows], ref, 0, H, "split T=%d norm=%s" % (T, norm))
 
 
 # --------------------------------------------------------------------------
