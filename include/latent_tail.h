@@ -94,7 +94,8 @@ extern "C" {
  * input), LT_ERR_UNSUPPORTED (L outside 8..LT_MAX_L or not a multiple of 8, a
  * misaligned pointer), LT_ERR_NO_MEMORY (the scratch of the T > skinny path
  * could not grow, or would have to grow while `stream` is being captured into
- * a graph), or LT_ERR_HIP.  T == 0 or n == 0 returns LT_OK with nothing
+ * a graph; calls with one partial and norm_w == NULL use no scratch), or
+ * LT_ERR_HIP.  T == 0 or n == 0 returns LT_OK with nothing
  * launched ([PR50383 Key source snippets]: an empty batch is a legal state).
  */
 LT_API int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
@@ -145,7 +146,8 @@ LT_API const char *lt_status_string(int status);
 /*
  * lt_reserve -- pre-size the library-owned scratch used by calls with
  * T > skinny_max on `stream` of the current device: a [max_T][L] bf16 latent
- * buffer.  Calls that then fit never allocate, so they can be captured into a
+ * buffer (calls with one partial and norm_w == NULL multiply the partial in
+ * place and need none).  Calls that then fit never allocate, so they can be captured into a
  * HIP graph ([PR50593 Implementation, item 4]: graph capture and replay at
  * varying shapes is part of the validation there).  The buffer belongs to
  * (device, stream) and lives until lt_release_scratch or process exit.
@@ -173,7 +175,8 @@ LT_API int64_t lt_get_skinny_max_tokens(void);
 /*
  * lt_path_for -- which path a call with these sizes takes:
  * 0 = nothing launched (T == 0 or n == 0), 1 = weight-streaming (skinny),
- * 2 = sum+RMSNorm kernel then MFMA GEMM.  Host-only, launches nothing.
+ * 2 = sum+RMSNorm kernel then MFMA GEMM (the GEMM alone for one partial with
+ * norm_w == NULL).  Host-only, launches nothing.
  */
 LT_API int lt_path_for(int64_t T, int64_t n);
 
