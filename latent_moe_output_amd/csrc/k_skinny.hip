@@ -22,7 +22,9 @@
 //    drain the W stream), then the norm weight, then all of the workgroup's
 //    W chunks: the whole W share is in flight while the latent is
 //    normalised, and the read-modify-write of the window adds no memory
-//    round trip at the end.
+//    round trip at the end.  W is read exactly once per call, so its loads
+//    are marked non-temporal (T = 16: 5.83 vs 6.02 us back to back, T = 64:
+//    9.9 vs 10.6).
 //  * The latent is built in registers in the B-operand layout (token = lane
 //    % 16) by the shared tile code of lt_latent.h; splitting K over KW waves
 //    keeps each lane's share of the RMSNorm arithmetic small, and the norm's
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
                 const int c = 4 * KW * i + 4 * w + g;
                 const uint32_t off =
                     c < nchunk ? (uint32_t)((16 * jt + r) * L + c * 8) * 2u : LT_OOB;
-                wa[jt][i] = lt_buf_load16(rw, off);
+                wa[jt][i] = lt_buf_load16_nt(rw, off);
             }
     }
     if constexpr (ST) {

@@ -61,6 +61,16 @@ __device__ __forceinline__ u32x4_t lt_buf_load16(__amdgpu_buffer_rsrc_t r, uint3
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Cache-policy bit of buffer instructions: non-temporal (streamed data that
+// is not read again, e.g. the W window of a decode call).
+constexpr int LT_NT = 2;
+
+// The same load, marked non-temporal.
+__device__ __forceinline__ u32x4_t lt_buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, LT_NT));
+}
+
 // 1 / sqrt(mean square + eps) from the row's total of squares.
 __device__ __forceinline__ float lt_inv_rms(float total, float inv_L, float eps)
 {
