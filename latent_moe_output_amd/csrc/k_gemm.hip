@@ -520,7 +520,9 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
 // BT / 4 token rows: quarter 0 is fetched during stage nk - 2 (in place of A
 // of stage nk), quarters 1 and 2 during the last stage and quarter 3 once it
 // is done.  NKR = nk % 5 fixes, at compile time, the slot every stage and
-// quarter uses.  Same tile order, swizzles, K order and epilogue arithmetic
+// quarter uses.  The `out` tile is read and written once, so those loads and
+// stores are marked non-temporal (same box, alternating runs: T = 8192 about
+// 4-8 % faster).  Same tile order, swizzles, K order and epilogue arithmetic
 // as k_gemm, so the results are bit-identical to it.
 template <int BJ, int WGJ, int WGT, int GROUP_J, int NKR, bool KTAIL, bool RES>
 __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int64_t T, int L,
@@ -668,7 +670,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
             const int c = (idx % CPRE) ^ (r & (CPRE - 1));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rc, (lds_void *)(dst + idx0 * 16), 16,
-                (uint32_t)(((int64_t)r * ld_out + j0 + 8 * c) * 2), 0, 0, 0);
+                (uint32_t)(((int64_t)r * ld_out + j0 + 8 * c) * 2), 0, 0, LT_NT);
         }
     };
 
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
                     qb + rh * (BJ * 2) + ((c ^ (r & (CPRE - 1))) << 4));
                 if (j + 8 <= n) {
                     __builtin_amdgcn_raw_buffer_store_b128(
-                        v, rc, (uint32_t)(((int64_t)r * ld_out + j) * 2), 0, 0);
+                        v, rc, (uint32_t)(((int64_t)r * ld_out + j) * 2), 0, LT_NT);
                     if constexpr (RES) {
                         u32x4_t rv;
 #pragma unroll
