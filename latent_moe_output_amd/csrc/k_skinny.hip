@@ -12,19 +12,28 @@
 //    workgroup needs, are fetched as few times as possible.  Its KW waves
 //    split the latent width: chunk c (8 elements) belongs to wave
 //    (c / 4) % KW, lane group c % 4, step c / (4*KW).  Each lane's W chunks
-//    are loaded straight into registers in the A-operand layout of
-//    v_mfma_f32_16x16x32_bf16 (row = lane % 16, 8 consecutive k per lane), so
-//    W never passes through LDS.
+//    are needed in the A-operand layout of v_mfma_f32_16x16x32_bf16 (row =
+//    lane % 16, 8 consecutive k per lane).  Up to 32 tokens (WS) the block's
+//    W rows are copied into LDS as whole lines by direct-to-LDS loads, in the
+//    staged layout of lt_latent.h, and read back in that layout: a load in
+//    the operand layout touches 16 rows at one 64-byte offset, which the
+//    vector L1 moves at about a third of the rate of whole lines (T = 1:
+//    5.41 vs 5.69 us back to back, bit-identical).  For 33..64 tokens the
+//    staged latent leaves no room, and W is loaded into registers directly.
 //  * The out values the epilogue will add to are fetched first, then the
 //    latent (one partial: copied into LDS as whole lines and read back in the
-//    operand layout, see lt_latent.h; several: loaded and summed in
-//    registers before anything else is issued, so the sum's waits never
-//    drain the W stream), then the norm weight, then all of the workgroup's
-//    W chunks: the whole W share is in flight while the latent is
-//    normalised, and the read-modify-write of the window adds no memory
-//    round trip at the end.  W is read exactly once per call, so its loads
-//    are marked non-temporal (T = 16: 5.83 vs 6.02 us back to back, T = 64:
-//    9.9 vs 10.6).
+//    operand layout, see lt_latent.h, only the 1 KB blocks that hold tokens
+//    below T, with the norm weight copied once per workgroup; several: loaded
+//    and summed in registers before anything else is issued, so the sum's
+//    waits never drain the W stream), then all of the workgroup's W chunks:
+//    the whole W share is in flight while the latent is normalised, and the
+//    read-modify-write of the window adds no memory round trip at the end.
+//    Every load instruction issued ahead of W delays the W stream by the
+//    time the CU's address unit spends on it; loading only the tokens that
+//    exist and the norm weight once took T = 1 from 5.41 to 5.17 us and
+//    T = 32 from 7.14 to 6.55.  W is read exactly once per call, so its
+//    loads are marked non-temporal (T = 16: 5.83 vs 6.02 us back to back,
+//    T = 64: 9.9 vs 10.6).
 //  * The latent is built in registers in the B-operand layout (token = lane
 //    % 16) by the shared tile code of lt_latent.h; splitting K over KW waves
 //    keeps each lane's share of the RMSNorm arithmetic small, and the norm's
@@ -44,7 +53,7 @@
 namespace lt {
 namespace {
 
-template <int NI, int TT, int JT, bool RES, bool ST>
+template <int NI, int TT, int JT, bool RES, bool ST, bool WS>
 __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part, int64_t pstride,
                                                     int P, int T, int L,
                                                     const u16 *__restrict__ norm_w, float eps,
@@ -69,6 +78,9 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
     constexpr int RED_BYTES = KW * JT * TT * 64 * 16;
     __shared__ __attribute__((aligned(1024))) char lds_u[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
     auto red_acc = reinterpret_cast<f32x4_t (*)[JT * TT][64]>(lds_u);
+    // W rows staged as whole lines (WS), in the same layout as the latent
+    __shared__ __attribute__((aligned(1024))) char lds_w[WS ? latent_stage_bytes<JT, NI>() : 16];
+    __shared__ __attribute__((aligned(1024))) char lds_nw[ST ? weight_stage_bytes<NI>() : 16];
 
     // this wave's epilogue fragment (w < JT*TT): token tile w % TT, row tile w / TT
     const bool has_epi = w < JT * TT;
@@ -86,20 +98,22 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
         opre = *reinterpret_cast<const u32x2_t *>(outn + (int64_t)te * ld_out + j0 + jl);
         if constexpr (RES) ppre = *reinterpret_cast<const u32x2_t *>(prefn + (int64_t)te * ld_pre + j0 + jl);
     }
-    u32x4_t sv[TT][NI];
-    if constexpr (ST) {
-        latent_stage<TT, NI>(part, T, L, lds_u);
+    u32x4_t sv[TT][NI], wv[NI];
+    if constexpr (ST) {   // token rows past T are never stored: skip them
+        latent_stage<TT, NI, 0, true>(part, T, L, lds_u);
+        if (norm_w) weight_stage<NI>(norm_w, L, lds_nw);
     } else {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) latent_load(part + (int64_t)16 * tt * L, T - 16 * tt, L, sv[tt]);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
             latent_sum(part + (int64_t)16 * tt * L, pstride, P, T - 16 * tt, L, sv[tt]);
+        if (norm_w) latent_load_weight(norm_w, L, wv);
     }
-    u32x4_t wv[NI];
-    if (norm_w) latent_load_weight(norm_w, L, wv);
     u32x4_t wa[JT][NI];
-    {
+    if constexpr (WS) {
+        latent_stage<JT, NI, LT_NT>(Wn + (int64_t)j0 * L, rows, L, lds_w);
+    } else {
         const __amdgpu_buffer_rsrc_t rw = lt_rsrc(Wn + (int64_t)j0 * L, (uint32_t)(rows * L) * 2u);
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
@@ -112,12 +126,12 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
             }
     }
     if constexpr (ST) {
-        // the staged tiles have landed once at most the norm-weight and W
+        // the staged tiles and norm weight have landed once at most the W
         // loads issued after them are in flight
-        if (norm_w) __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(NI + JT * NI));
-        else __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(JT * NI));
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(JT * NI));
         lt_lds_barrier();
         latent_from_lds<TT, NI>(lds_u, sv);
+        if (norm_w) weight_from_lds<NI>(lds_nw, wv);
         if (!norm_w) {   // the products below reuse the staging area
             __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));
             lt_lds_barrier();
@@ -126,6 +140,11 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
 
     // 2. RMSNorm (its barrier waits for LDS only; W stays in flight)
     if (norm_w) latent_norm<TT, NI>(sv, wv, eps, inv_L, red_ss);
+    if constexpr (WS) {   // every wave's share of the W rows has landed
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+        lt_lds_barrier();
+        latent_from_lds<JT, NI>(lds_w, wa);
+    }
 
     // 3. projection on the matrix cores: D[j][t] += W[j][k] * y[t][k]
     f32x4_t acc[JT][TT];
@@ -204,8 +223,10 @@ hipError_t launch_nt(const u16 *part, int64_t pstride, int P, int T, int L, cons
     const u16 *pre = res ? res->prefix : nullptr;
     u16 *rsd = res ? res->resid : nullptr;
     const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
+    // W rows through LDS while the staged latent and W fit in it
+    constexpr bool WS = TT <= 2 && NI <= 4;
 #define LT_SKINNY_LAUNCH(R, S)                                                                  \
-    hipLaunchKernelGGL((k_skinny<NI, TT, JT, R, S>), grid, block, 0, stream, part, pstride, P, T, \
+    hipLaunchKernelGGL((k_skinny<NI, TT, JT, R, S, WS>), grid, block, 0, stream, part, pstride, P, T, \
                        L, norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8, pre, ldp,  \
                        rsd, ldr)
     // one partial: the latent tiles are staged through LDS as whole lines

@@ -78,24 +78,31 @@ template <int TT, int NI>
 constexpr int latent_stage_bytes() { return 16 * TT * NI * 512; }
 
 // Issues the copy of tokens [0, min(Tv, 16*TT)) of partial 0 (row stride L)
-// into the staged layout: TT*NI direct loads per wave, all KW waves taking
-// part.  The caller waits for them (vmcnt) and runs a workgroup barrier
-// before latent_from_lds.
-template <int TT, int NI>
+// into the staged layout: up to TT*NI direct loads per wave, all KW waves
+// taking part, with cache policy AUX.  The caller waits for them (vmcnt) and
+// runs a workgroup barrier before latent_from_lds.  The A operand of
+// v_mfma_f32_16x16x32_bf16 has the same per-lane layout as the B operand
+// (row = lane % 16), so W rows can be staged and read back the same way.
+// With SKIP, 1 KB blocks that start at or past row Tv are not loaded: those
+// rows keep whatever the LDS held.  That is harmless wherever rows >= Tv are
+// never stored: every output of an MFMA depends on one row of each operand,
+// so stale rows reach only outputs of their own row.
+template <int TT, int NI, int AUX = 0, bool SKIP = false>
 __device__ __forceinline__ void latent_stage(const u16 *__restrict__ tile, int Tv, int L, char *lds)
 {
     static_assert((NI & (NI - 1)) == 0, "slots per row must be a power of two");
     constexpr int SPR = 32 * NI;                  // 16-byte slots per staged row
-    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const __amdgpu_buffer_rsrc_t r = lt_rsrc(tile, latent_tile_bytes(Tv < 16 * TT ? Tv : 16 * TT, L));
 #pragma unroll
     for (int k = 0; k < TT * NI; ++k) {
         const int m = KW * k + w;                 // 1 KB block of the staging area
+        if (SKIP && 64 * m / SPR >= Tv) continue;   // wave-uniform
         const int slot = 64 * m + l;
         const int row = slot / SPR, c = (slot % SPR) ^ (row & 15);
         const uint32_t off = c < (L >> 3) ? (uint32_t)(row * L + c * 8) * 2u : LT_OOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void *)(lds + 1024 * m), 16, off, 0, 0, 0);
+            r, (__attribute__((address_space(3))) void *)(lds + 1024 * m), 16, off, 0, 0, AUX);
     }
 }
 
@@ -144,6 +151,35 @@ __device__ __forceinline__ void latent_load_weight(const u16 *__restrict__ norm_
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         wv[i] = lt_buf_load16(r, (uint32_t)(4 * KW * i + 4 * w + g) * 16u);
+}
+
+// The norm weight staged in LDS: its first 512*NI bytes in natural order
+// (zeros past the row end), copied by the first max(1, NI/2) waves with one
+// 1 KB direct load each instead of NI loads in every wave.  The caller waits
+// (vmcnt) and runs a workgroup barrier before weight_from_lds.
+template <int NI>
+constexpr int weight_stage_bytes() { return NI >= 2 ? 512 * NI : 1024; }
+
+template <int NI>
+__device__ __forceinline__ void weight_stage(const u16 *__restrict__ norm_w, int L, char *lds)
+{
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= weight_stage_bytes<NI>() / 1024) return;
+    const __amdgpu_buffer_rsrc_t r = lt_rsrc(norm_w, (uint32_t)L * 2u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)(lds + 1024 * w), 16,
+        (uint32_t)(1024 * w + 16 * l), 0, 0, 0);
+}
+
+// This lane's chunks of the staged norm weight (what latent_load_weight loads).
+template <int NI>
+__device__ __forceinline__ void weight_from_lds(const char *lds, u32x4_t (&wv)[NI])
+{
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = l >> 4;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        wv[i] = *reinterpret_cast<const u32x4_t *>(lds + (4 * KW * i + 4 * w + g) * 16);
 }
 
 // Adds partials 1..P-1 (stride pstride elements) in fp32, p ascending, and
