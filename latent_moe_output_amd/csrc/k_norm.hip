@@ -25,22 +25,27 @@ __global__ __launch_bounds__(64 * KW) void k_sum_rmsnorm(const u16 *__restrict__
 {
     __shared__ float red[1][KW * 16];
     __shared__ __attribute__((aligned(1024))) char lds_t[latent_stage_bytes<1, NI>()];
+    __shared__ __attribute__((aligned(1024))) char lds_nw[ST ? weight_stage_bytes<NI>() : 16];
     const int64_t t0 = (int64_t)blockIdx.x * 16;
     const int Tv = (int)min((int64_t)16, T - t0);
     const u16 *tile = part + t0 * L;
 
-    // one partial: the tile is copied into LDS as whole lines (ST); several:
-    // loaded and summed in registers
+    // one partial: the tile (its rows below Tv) and the norm weight are
+    // copied into LDS as whole lines (ST); several: loaded and summed in
+    // registers
     u32x4_t sv[1][NI], wv[NI];
-    if constexpr (ST) latent_stage<1, NI>(tile, Tv, L, lds_t);
-    else latent_load(tile, Tv, L, sv[0]);
-    if (norm_w) latent_load_weight(norm_w, L, wv);
     if constexpr (ST) {
-        if (norm_w) __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(NI));
-        else __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+        latent_stage<1, NI, 0, true>(tile, Tv, L, lds_t);
+        if (norm_w) weight_stage<NI>(norm_w, L, lds_nw);
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
         lt_lds_barrier();
-        if (norm_w) latent_from_lds<1, NI>(lds_t, sv);
+        if (norm_w) {
+            latent_from_lds<1, NI>(lds_t, sv);
+            weight_from_lds<NI>(lds_nw, wv);
+        }
     } else {
+        latent_load(tile, Tv, L, sv[0]);
+        if (norm_w) latent_load_weight(norm_w, L, wv);
         latent_sum(tile, pstride, P, Tv, L, sv[0]);
     }
     // the normalised tile goes back into the staged layout (each slot is
