@@ -83,12 +83,17 @@ __device__ __forceinline__ int swz8(int r)
     return ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
 }
 
+// Argument order: everything the tile set-up needs comes first, within the
+// 14 argument dwords that are preloaded into scalar registers at wave launch
+// (the library is built with kernel-argument preloading); the residual
+// pointers, read only by the epilogue, come last.
 template <int BJ, int BT, int WGJ, int WGT, int NS, int GROUP_J, bool KTAIL, bool EPI_LDS, bool RES>
-__global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__ Y, int64_t T, int L,
-                                                         const u16 *__restrict__ Wn, int n,
+__global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__ Y, int ntj, int ntt,
+                                                         int64_t T, int L, int n,
+                                                         const u16 *__restrict__ Wn,
                                                          u16 *__restrict__ outn, int64_t ld_out,
-                                                         int ntj, int ntt, const u16 *prefn,
-                                                         int64_t ld_pre, u16 *resn, int64_t ld_res)
+                                                         const u16 *prefn, int64_t ld_pre,
+                                                         u16 *resn, int64_t ld_res)
 {
     constexpr int NW = WGJ * WGT;               // waves, in a WGJ x WGT grid
     constexpr int NT = 64 * NW;                 // threads
@@ -525,11 +530,12 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
 // 4-8 % faster).  Same tile order, swizzles, K order and epilogue arithmetic
 // as k_gemm, so the results are bit-identical to it.
 template <int BJ, int WGJ, int WGT, int GROUP_J, int NKR, bool KTAIL, bool RES>
-__global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int64_t T, int L,
-                                                              const u16 *__restrict__ Wn, int n,
+__global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int ntj, int ntt,
+                                                              int64_t T, int L, int n,
+                                                              const u16 *__restrict__ Wn,
                                                               u16 *__restrict__ outn, int64_t ld_out,
-                                                              int ntj, int ntt, const u16 *prefn,
-                                                              int64_t ld_pre, u16 *resn, int64_t ld_res)
+                                                              const u16 *prefn, int64_t ld_pre,
+                                                              u16 *resn, int64_t ld_res)
 {
     constexpr int BT = BJ;
     constexpr int NW = WGJ * WGT;
@@ -903,7 +909,7 @@ hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16
     const bool kt = L % BK != 0;
 #define LT_RING(NKR, KT, R)                                                                  \
     hipLaunchKernelGGL((k_gemm_ring<BJ, WGJ, WGT, GROUP_J, NKR, KT, R>), grid, block, 0, stream, \
-                       y, T, L, Wn, n, outn, ld_out, ntj, (int)ntt, pre, ldp, rsd, ldr)
+                       y, ntj, (int)ntt, T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
 #define LT_RING_K(NKR)                                                                       \
     do {                                                                                     \
         if (kt) { if (res) LT_RING(NKR, true, true); else LT_RING(NKR, true, false); }       \
@@ -942,7 +948,7 @@ hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 
     const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
 #define LT_GEMM_LAUNCH(KT, EPI, R)                                                           \
     hipLaunchKernelGGL((k_gemm<BJ, BT, WGJ, WGT, NS, GROUP_J, KT, EPI, R>), grid, block, 0, stream, \
-                       y, T, L, Wn, n, outn, ld_out, ntj, (int)ntt, pre, ldp, rsd, ldr)
+                       y, ntj, (int)ntt, T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
 #define LT_GEMM_LAUNCH_R(KT, EPI)                                                            \
     do {                                                                                     \
         if (res) LT_GEMM_LAUNCH(KT, EPI, true); else LT_GEMM_LAUNCH(KT, EPI, false);        \

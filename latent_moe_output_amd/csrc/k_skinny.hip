@@ -53,15 +53,21 @@
 namespace lt {
 namespace {
 
+// Argument order: what the loads ahead of the W stream need (the out
+// prefetch, the staged latent, the norm weight, the W rows) fills the 14
+// argument dwords that are preloaded into scalar registers at wave launch;
+// rw_vec packs the rows per block (bits 0..7) and the 8-byte out flag (bit 8).
 template <int NI, int TT, int JT, bool RES, bool ST, bool WS>
-__global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part, int64_t pstride,
-                                                    int P, int T, int L,
-                                                    const u16 *__restrict__ norm_w, float eps,
-                                                    float inv_L, const u16 *__restrict__ Wn, int n,
-                                                    int RW, u16 *__restrict__ outn, int64_t ld_out,
-                                                    int vec8, const u16 *prefn, int64_t ld_pre,
-                                                    u16 *resn, int64_t ld_res)
+__global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part,
+                                                    const u16 *__restrict__ Wn,
+                                                    u16 *__restrict__ outn,
+                                                    const u16 *__restrict__ norm_w, int64_t ld_out,
+                                                    int T, int L, int n, int rw_vec,
+                                                    int64_t pstride, int P, float eps, float inv_L,
+                                                    const u16 *prefn, int64_t ld_pre, u16 *resn,
+                                                    int64_t ld_res)
 {
+    const int RW = rw_vec & 0xFF, vec8 = rw_vec >> 8;
     static_assert(JT * TT <= KW, "one epilogue fragment per wave");
     const int l = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -226,9 +232,9 @@ hipError_t launch_nt(const u16 *part, int64_t pstride, int P, int T, int L, cons
     // W rows through LDS while the staged latent and W fit in it
     constexpr bool WS = TT <= 2 && NI <= 4;
 #define LT_SKINNY_LAUNCH(R, S)                                                                  \
-    hipLaunchKernelGGL((k_skinny<NI, TT, JT, R, S, WS>), grid, block, 0, stream, part, pstride, P, T, \
-                       L, norm_w, eps, 1.0f / (float)L, Wn, n, RW, outn, ld_out, vec8, pre, ldp,  \
-                       rsd, ldr)
+    hipLaunchKernelGGL((k_skinny<NI, TT, JT, R, S, WS>), grid, block, 0, stream, part, Wn, outn,   \
+                       norm_w, ld_out, T, L, n, RW | (vec8 << 8), pstride, P, eps, 1.0f / (float)L,  \
+                       pre, ldp, rsd, ldr)
     // one partial: the latent tiles are staged through LDS as whole lines
     if (res) {
         if (P == 1) LT_SKINNY_LAUNCH(true, true); else LT_SKINNY_LAUNCH(true, false);
