@@ -18,8 +18,10 @@
 //    staged layout of lt_latent.h, and read back in that layout: a load in
 //    the operand layout touches 16 rows at one 64-byte offset, which the
 //    vector L1 moves at about a third of the rate of whole lines (T = 1:
-//    5.41 vs 5.69 us back to back, bit-identical).  For 33..64 tokens the
-//    staged latent leaves no room, and W is loaded into registers directly.
+//    5.41 vs 5.69 us back to back, bit-identical).  For 33..64 tokens with
+//    one partial the latent is staged two tiles at a time through one
+//    64 KB area (tiles 2 and 3 are fetched once tiles 0 and 1 are in
+//    registers, after the W rows), so W fits in LDS beside it.
 //  * The out values the epilogue will add to are fetched first, then the
 //    latent (one partial: copied into LDS as whole lines and read back in the
 //    operand layout, see lt_latent.h, only the 1 KB blocks that hold tokens
@@ -80,7 +82,11 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
     __shared__ float red_ss[TT][KW * 16];
     // The staged latent tiles (one partial, ST) and, once the latent is in
     // registers, the per-wave partial products share one LDS area.
-    constexpr int STAGE_BYTES = ST ? latent_stage_bytes<TT, NI>() : 0;
+    // SPLIT: four token tiles with one partial are staged two at a time
+    // through one half-size area, so that W fits in LDS next to them
+    constexpr bool SPLIT = ST && TT == 4;
+    constexpr int TS = SPLIT ? 2 : TT;          // tiles per staging pass
+    constexpr int STAGE_BYTES = ST ? latent_stage_bytes<TS, NI>() : 0;
     constexpr int RED_BYTES = KW * JT * TT * 64 * 16;
     __shared__ __attribute__((aligned(1024))) char lds_u[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
     auto red_acc = reinterpret_cast<f32x4_t (*)[JT * TT][64]>(lds_u);
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
     }
     u32x4_t sv[TT][NI], wv[NI];
     if constexpr (ST) {   // token rows past T are never stored: skip them
-        latent_stage<TT, NI, 0, true>(part, T, L, lds_u);
+        latent_stage<TS, NI, 0, true>(part, T, L, lds_u);
         if (norm_w) weight_stage<NI>(norm_w, L, lds_nw);
     } else {
 #pragma unroll
@@ -136,19 +142,39 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
         // loads issued after them are in flight
         __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(JT * NI));
         lt_lds_barrier();
-        latent_from_lds<TT, NI>(lds_u, sv);
+        latent_from_lds<TS, NI>(lds_u, *reinterpret_cast<u32x4_t (*)[TS][NI]>(&sv[0]));
         if (norm_w) weight_from_lds<NI>(lds_nw, wv);
-        if (!norm_w) {   // the products below reuse the staging area
+        if (SPLIT || !norm_w) {   // the staging area is reused (tiles 2, 3 / the products)
             __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));
             lt_lds_barrier();
         }
+        // tiles 2 and 3 follow the W rows; the first two tiles' norm runs
+        // while both are in flight
+        if constexpr (SPLIT)
+            latent_stage<2, NI, 0, true>(part + (int64_t)32 * L, T - 32, L, lds_u);
     }
 
     // 2. RMSNorm (its barrier waits for LDS only; W stays in flight)
-    if (norm_w) latent_norm<TT, NI>(sv, wv, eps, inv_L, red_ss);
-    if constexpr (WS) {   // every wave's share of the W rows has landed
-        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+    if constexpr (SPLIT) {
+        if (norm_w)
+            latent_norm<2, NI>(*reinterpret_cast<u32x4_t (*)[2][NI]>(&sv[0]), wv, eps, inv_L, red_ss);
+        __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));   // tiles 2, 3 and the W rows
         lt_lds_barrier();
+        latent_from_lds<2, NI>(lds_u, *reinterpret_cast<u32x4_t (*)[2][NI]>(&sv[2]));
+        if (norm_w)
+            latent_norm<2, NI>(*reinterpret_cast<u32x4_t (*)[2][NI]>(&sv[2]), wv, eps, inv_L, red_ss + 2);
+        else {   // the products below reuse the staging area
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(63));
+            lt_lds_barrier();
+        }
+    } else {
+        if (norm_w) latent_norm<TT, NI>(sv, wv, eps, inv_L, red_ss);
+    }
+    if constexpr (WS) {   // every wave's share of the W rows has landed
+        if constexpr (!SPLIT) {
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
+            lt_lds_barrier();
+        }
         latent_from_lds<JT, NI>(lds_w, wa);
     }
 
@@ -230,7 +256,7 @@ hipError_t launch_nt(const u16 *part, int64_t pstride, int P, int T, int L, cons
     u16 *rsd = res ? res->resid : nullptr;
     const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
     // W rows through LDS while the staged latent and W fit in it
-    constexpr bool WS = TT <= 2 && NI <= 4;
+    constexpr bool WS = NI <= 4;
 #define LT_SKINNY_LAUNCH(R, S)                                                                  \
     hipLaunchKernelGGL((k_skinny<NI, TT, JT, R, S, WS>), grid, block, 0, stream, part, Wn, outn,   \
                        norm_w, ld_out, T, L, n, RW | (vec8 << 8), pstride, P, eps, 1.0f / (float)L,  \
