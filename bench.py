@@ -29,8 +29,10 @@ the events; `graph_call_us` is each T on its own: its rotation sets captured
 into one graph (each call on its own W copy) and replayed, elapsed time per
 call.  `roofline` is for the dominant kernel (k_gemm_ring at
 T=8192); `roofline_skinny` for the weight-streaming kernel at T <= 16;
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the T=8192
-call on this host's cores.  `roofline.traffic` is the GEMM's HBM bytes per
+`configs` times the column-shard workloads (T=256 with 8 partials, T=8191
+with 4 partials, with and without the norm, 896-column windows) against
+their rooflines.  `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the T=8192 call on this host's cores.  `roofline.traffic` is the GEMM's HBM bytes per
 launch from the committed rocprofv3 counter summary under profiles/, or null
 once the GEMM sources differ from the ones those counters were taken on.
 """
@@ -245,6 +247,77 @@ def residual_pass(binding, hip, stream, sh, sets, wpool, norm_w, call_kern, reps
                 "extra_bytes": 4 * T * H,
             }
             del pre, rsd
+    return res
+
+
+CONFIG_RUNS = ("shard", "ragged", "ragged_nonorm")
+
+
+def configs_pass(binding, hip, stream, sh, wpool, reps=10):
+    """The column-shard workloads at their real shapes (not part of `value`):
+    the 8-partial shard (T=256, window of 896 columns) and the ragged prefill
+    shard (T=8191, 4 partials, window of 896 columns) with and without the
+    norm.  Inputs drawn on the device (same distributions as the host
+    generator; the ragged workload's +-1e4 outliers are left out, they do not
+    change the work).  Each call reads its own W copy and rotates its
+    partials/out sets; back-to-back time per call from a replayed graph."""
+    import torch
+
+    from latent_moe_output_amd import synth
+
+    res = {}
+    for name in CONFIG_RUNS:
+        wl = synth.WORKLOADS[name]
+        per = 2 * wl.P * wl.T * wl.L + 2 * wl.T * wl.ld_out
+        R = int(min(16, max(2, math.ceil(ROTATE_BYTES / per))))
+        with torch.cuda.stream(stream):
+            sets = [synth.generate_device(wl, seed=s) for s in range(R)]
+        torch.cuda.synchronize()
+        nw = sets[0]["norm_w"]
+
+        def one(i):
+            d = sets[i % R]
+            return binding.lt_latent_tail(d["partials"], wl.P, wl.T, wl.L, nw, wl.eps,
+                                          wpool[(5 * i) % len(wpool)], wl.H, wl.c0, wl.n,
+                                          d["out"], wl.ld_out, sh)
+
+        for i in range(R):
+            binding.check(one(i))
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(R):
+                binding.check(one(i))
+        with torch.cuda.stream(stream):
+            g.replay()
+            a, b = hip.event(), hip.event()
+            hip.record(a, sh)
+            for _ in range(reps):
+                g.replay()
+            hip.record(b, sh)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(a, b) * 1e3 / (reps * R)
+        hip.destroy(a)
+        hip.destroy(b)
+        f = 2 * wl.T * wl.L * wl.n
+        byt = 2 * wl.n * wl.L + 2 * wl.P * wl.T * wl.L + 4 * wl.T * wl.n + (2 * wl.L if wl.norm else 0)
+        roof_us = max(byt / HBM_PEAK, f / MFMA_BF16_PEAK) * 1e6
+        res[name] = {
+            "T": wl.T, "n_partials": wl.P, "c0": wl.c0, "n": wl.n, "ld_out": wl.ld_out,
+            "norm": wl.norm,
+            "path": "skinny" if binding.lt_path_for(wl.T, wl.n) == 1 else "sum+norm, gemm",
+            "call_us": round(us, 3),
+            "tflops": round(f / us / 1e6, 2),
+            "alg_gbps": round(byt / us / 1e3, 1),
+            "alg_bytes": byt,
+            "roofline_us": round(roof_us, 3),
+            "bound": "hbm" if byt / HBM_PEAK > f / MFMA_BF16_PEAK else "mfma",
+            "frac_of_roofline": round(roof_us / us, 3),
+            "timing": "graph of %d calls (own W copy and input set each) replayed %d times"
+                      % (R, reps),
+        }
+        del sets, g
+        torch.cuda.synchronize()
     return res
 
 
@@ -529,6 +602,8 @@ def main():
                   "between launches)" % NB,
     }
 
+    configs = configs_pass(binding, hip, stream, sh, wpool)
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -557,6 +632,7 @@ def main():
         "roofline": roofline,
         "roofline_skinny": roofline_skinny,
         "residual": residual,
+        "configs": configs,
         "context": context,
     }
     if not args.no_cpu:
