@@ -281,14 +281,17 @@ def test_shards_concatenate_bit_exact(T):
     np.testing.assert_array_equal(host(part.out), host(full.out))
 
 
-@pytest.mark.parametrize("T,H,norm", [(7, 512, True), (130, 512, True), (130, 512, False),
-                                      (1000, 1024, False), (2048, 7168, False),
-                                      (2048, 7168, True)])
+@pytest.mark.parametrize("T,H,norm", [(7, 512, True), (20, 7168, True), (48, 512, True),
+                                      (48, 512, False), (64, 7168, True), (130, 512, True),
+                                      (130, 512, False), (1000, 1024, False),
+                                      (2048, 7168, False), (2048, 7168, True)])
 def test_split_partials_bit_exact(T, H, norm):
     """[X, Y, -Y] and [X/2, X/2] give the same bits as [X].  With the norm off
     the large-token path multiplies one partial in place and sums several
-    first, so this also ties the two routes together; the one-partial result
-    is checked against the oracle on sampled rows."""
+    first, so this also ties the two routes together; on the weight-streaming
+    path (T <= 64) one partial is staged through LDS (two tiles at a time
+    past 32 tokens) while several are summed in registers.  The one-partial
+    result is checked against the oracle on sampled rows."""
     from oracle import oracle
 
     wl = synth.Workload("split", T=T, L=1024, H=H, P=1, c0=0, n=H, ld_out=H, norm=norm)
