@@ -18,10 +18,12 @@ namespace lt {
 namespace {
 
 template <int NI, bool ST>
-__global__ __launch_bounds__(64 * KW) void k_sum_rmsnorm(const u16 *__restrict__ part,
+// `y` may be `part` itself with one partial: every workgroup has copied its
+// rows into LDS (and waited for them) before it writes them.
+__global__ __launch_bounds__(64 * KW) void k_sum_rmsnorm(const u16 *part,
                                                          int64_t pstride, int P, int64_t T, int L,
                                                          const u16 *__restrict__ norm_w, float eps,
-                                                         float inv_L, u16 *__restrict__ y)
+                                                         float inv_L, u16 *y)
 {
     __shared__ float red[1][KW * 16];
     __shared__ __attribute__((aligned(1024))) char lds_t[latent_stage_bytes<1, NI>()];
@@ -71,6 +73,35 @@ __global__ __launch_bounds__(64 * KW) void k_sum_rmsnorm(const u16 *__restrict__
     }
 }
 
+// s = bf16(sum_p part[p]) elementwise, fp32 accumulation in ascending p (the
+// order latent_sum uses, so the result is the same bits): 8 elements per
+// thread, all P loads of a thread issued together, whole lines per wave.
+__global__ __launch_bounds__(256) void k_sum_partials(const u16 *__restrict__ part, int64_t pstride,
+                                                      int P, int64_t count, u16 *__restrict__ s)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= count) return;
+    const u16 *src = part + i;
+    float acc[8];
+    lt_unpack8(*reinterpret_cast<const u32x4_t *>(src), acc);
+    constexpr int B = 8;                     // partials in flight per thread
+    for (int p = 1; p < P; p += B) {
+        u32x4_t x[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            if (p + b < P) x[b] = *reinterpret_cast<const u32x4_t *>(src + (int64_t)(p + b) * pstride);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (p + b >= P) break;
+            float f[8];
+            lt_unpack8(x[b], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = acc[e] + f[e];
+        }
+    }
+    *reinterpret_cast<u32x4_t *>(s + i) = lt_pack8(acc);
+}
+
 template <int NI>
 hipError_t launch_ni(const u16 *part, int64_t pstride, int P, int64_t T, int L,
                      const u16 *norm_w, float eps, u16 *y, hipStream_t stream)
@@ -86,6 +117,15 @@ hipError_t launch_ni(const u16 *part, int64_t pstride, int P, int64_t T, int L,
 }
 
 }  // namespace
+
+hipError_t launch_sum_partials(const uint16_t *part, int64_t pstride, int P, int64_t count,
+                               uint16_t *s, hipStream_t stream)
+{
+    const int64_t threads = (count + 7) / 8;
+    hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, part, pstride, P, count, s);
+    return hipGetLastError();
+}
 
 hipError_t launch_sum_rmsnorm(const uint16_t *part, int64_t pstride, int P, int64_t T, int L,
                               const uint16_t *norm_w, float eps, uint16_t *y,
