@@ -281,20 +281,26 @@ def test_shards_concatenate_bit_exact(T):
     np.testing.assert_array_equal(host(part.out), host(full.out))
 
 
-@pytest.mark.parametrize("T,H,norm", [(7, 512, True), (20, 7168, True), (48, 512, True),
-                                      (48, 512, False), (64, 7168, True), (130, 512, True),
-                                      (130, 512, False), (1000, 1024, False),
-                                      (2048, 7168, False), (2048, 7168, True)])
-def test_split_partials_bit_exact(T, H, norm):
+@pytest.mark.parametrize("T,H,norm,L", [(7, 512, True, 1024), (20, 7168, True, 1024),
+                                        (48, 512, True, 1024), (48, 512, False, 1024),
+                                        (64, 7168, True, 1024), (130, 512, True, 1024),
+                                        (130, 512, False, 1024), (300, 512, True, 264),
+                                        (1000, 1024, False, 1024), (1023, 512, True, 1024),
+                                        (1023, 512, False, 1024), (1024, 512, True, 1024),
+                                        (2048, 7168, False, 1024), (2048, 7168, True, 1024)])
+def test_split_partials_bit_exact(T, H, norm, L):
     """[X, Y, -Y] and [X/2, X/2] give the same bits as [X].  With the norm off
     the large-token path multiplies one partial in place and sums several
-    first, so this also ties the two routes together; on the weight-streaming
-    path (T <= 64) one partial is staged through LDS (two tiles at a time
-    past 32 tokens) while several are summed in registers.  The one-partial
-    result is checked against the oracle on sampled rows."""
+    first, so this also ties the two routes together; below 1024 tokens
+    several partials are summed by their own kernel before the norm, from
+    1024 on inside the norm kernel (both sides of that threshold are here);
+    on the weight-streaming path (T <= 64) one partial is staged through LDS
+    (two tiles at a time past 32 tokens) while several are summed in
+    registers.  The one-partial result is checked against the oracle on
+    sampled rows."""
     from oracle import oracle
 
-    wl = synth.Workload("split", T=T, L=1024, H=H, P=1, c0=0, n=H, ld_out=H, norm=norm)
+    wl = synth.Workload("split", T=T, L=L, H=H, P=1, c0=0, n=H, ld_out=H, norm=norm)
     d = synth.generate(wl, seed=7)
     X = d["partials"]
     Y = synth.generate(wl, seed=8)["partials"]
@@ -303,7 +309,7 @@ def test_split_partials_bit_exact(T, H, norm):
     for parts in (X, np.concatenate([X, Y, Y ^ 0x8000]), np.concatenate([half, half])):
         dd = dict(d, partials=parts)
         di = DevInputs(dd)
-        say("split partials T=%d H=%d norm=%s P=%d" % (T, H, norm, parts.shape[0]))
+        say("split partials T=%d H=%d L=%d norm=%s P=%d" % (T, H, L, norm, parts.shape[0]))
         binding.check(di.call(wl))
         _sync()
         results.append(host(di.out))
