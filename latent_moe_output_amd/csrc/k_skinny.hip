@@ -13,15 +13,16 @@
 //    split the latent width: chunk c (8 elements) belongs to wave
 //    (c / 4) % KW, lane group c % 4, step c / (4*KW).  Each lane's W chunks
 //    are needed in the A-operand layout of v_mfma_f32_16x16x32_bf16 (row =
-//    lane % 16, 8 consecutive k per lane).  Up to 32 tokens (WS) the block's
-//    W rows are copied into LDS as whole lines by direct-to-LDS loads, in the
-//    staged layout of lt_latent.h, and read back in that layout: a load in
-//    the operand layout touches 16 rows at one 64-byte offset, which the
-//    vector L1 moves at about a third of the rate of whole lines (T = 1:
-//    5.41 vs 5.69 us back to back, bit-identical).  For 33..64 tokens with
-//    one partial the latent is staged two tiles at a time through one
-//    64 KB area (tiles 2 and 3 are fetched once tiles 0 and 1 are in
-//    registers, after the W rows), so W fits in LDS beside it.
+//    lane % 16, 8 consecutive k per lane).  While the latent is at most 1024
+//    wide (WS) the block's W rows are copied into LDS as whole lines by
+//    direct-to-LDS loads, in the staged layout of lt_latent.h, and read back
+//    in that layout: a load in the operand layout touches 16 rows at one
+//    64-byte offset, which the vector L1 moves at about a third of the rate
+//    of whole lines (T = 1: 5.41 vs 5.69 us back to back, bit-identical).
+//    For 33..64 tokens with one partial the latent is staged two tiles at a
+//    time through one 64 KB area (tiles 2 and 3 are fetched once tiles 0 and
+//    1 are in registers, after the W rows), so W fits in LDS beside it; wider
+//    latents leave no room and load W straight into registers.
 //  * The out values the epilogue will add to are fetched first, then the
 //    latent (one partial: copied into LDS as whole lines and read back in the
 //    operand layout, see lt_latent.h, only the 1 KB blocks that hold tokens
