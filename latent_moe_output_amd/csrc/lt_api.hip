@@ -7,7 +7,10 @@
 // Implementation, item 1], reduced to the two single-GPU paths:
 //   T <= skinny_max  -> one weight-streaming launch per 64 tokens (32 when
 //                       L > 1024) (k_skinny)
-//   T >  skinny_max  -> k_sum_rmsnorm into a scratch latent, then k_gemm.
+//   T >  skinny_max  -> k_sum_rmsnorm into a scratch latent, then k_gemm
+//                       (several partials below 1024 tokens: k_sum_partials
+//                       into the scratch first, normalised there in place;
+//                       one partial without the norm: k_gemm reads it as is).
 // lt_latent_tail_residual runs the same path with the decoder layer's
 // residual update fused into the epilogue of the projection kernel.
 // The pages' own fallback is silent ([PR51253 Implementation, item 2]); a
