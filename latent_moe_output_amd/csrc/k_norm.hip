@@ -17,9 +17,9 @@
 namespace lt {
 namespace {
 
-template <int NI, bool ST>
 // `y` may be `part` itself with one partial: every workgroup has copied its
 // rows into LDS (and waited for them) before it writes them.
+template <int NI, bool ST>
 __global__ __launch_bounds__(64 * KW) void k_sum_rmsnorm(const u16 *part,
                                                          int64_t pstride, int P, int64_t T, int L,
                                                          const u16 *__restrict__ norm_w, float eps,
