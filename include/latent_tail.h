@@ -16,9 +16,13 @@
  *   - Every pointer is a DEVICE pointer on the current HIP device, owned by
  *     the caller; the library keeps no pointer after a call returns.
  *   - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
- *     NULL means the default stream).  No call synchronises the device or
- *     copies between host and device, except that growing the internal
- *     scratch buffer (see lt_reserve) synchronises `stream` first.
+ *     NULL means the default stream; hipStreamPerThread is the calling
+ *     thread's own stream).  No call synchronises the device or copies
+ *     between host and device; only lt_release_scratch synchronises, and
+ *     growing the internal scratch (see lt_reserve) calls hipMalloc.
+ *   - The library never reads or clears the caller's pending HIP error
+ *     state: launch failures come back as LT_ERR_HIP from the launch's own
+ *     status.
  *   - Argument errors are reported before anything is launched; in that case
  *     no device memory has been read or written.
  *   - The library is thread-safe.  Results are bit-identical from run to run
@@ -140,23 +144,47 @@ LT_API int lt_latent_tail_residual(const void *partials, int n_partials, int64_t
                                    const void *prefix, int64_t ld_prefix, void *resid,
                                    int64_t ld_resid, void *stream);
 
-/* Human-readable name of a status code (static storage, never NULL). */
+/*
+ * lt_status_string -- human-readable name of a status code (static storage,
+ * never NULL).  The pages' runner falls back silently, with one warning, when
+ * a precondition of the sharded tail fails ([PR51253 Implementation, item 2];
+ * [PR51253 Risks and impact, item 2] notes that this hides the lost
+ * optimisation), and [PR50383 Risks and impact] flags a missing divisibility
+ * check; a library cannot fall back to a path it does not own, so every
+ * failed precondition is a status code the caller can name and act on.
+ */
 LT_API const char *lt_status_string(int status);
 
 /*
  * lt_reserve -- pre-size the library-owned scratch used by calls with
  * T > skinny_max on `stream` of the current device: a [max_T][L] bf16 latent
  * buffer (calls with one partial and norm_w == NULL multiply the partial in
- * place and need none).  Calls that then fit never allocate, so they can be captured into a
- * HIP graph ([PR50593 Implementation, item 4]: graph capture and replay at
- * varying shapes is part of the validation there).  The buffer belongs to
- * (device, stream) and lives until lt_release_scratch or process exit.
+ * place and need none).  Calls that then fit never allocate, so they can be
+ * captured into a HIP graph ([PR50593 Implementation, item 4]: graph capture
+ * and replay at varying shapes is part of the validation there).  The buffer
+ * belongs to (device, stream) -- for hipStreamPerThread to (device, calling
+ * thread) -- and is shared by every call on that stream.
+ *
+ * Lifetime: a buffer is never freed while the library is loaded, except by
+ * lt_release_scratch.  When a later call on the same stream (outside capture)
+ * needs more, a larger buffer takes over and the old one is kept, so graphs
+ * captured earlier stay valid and keep using the buffer they captured.  A
+ * call under capture that would need to grow the buffer returns
+ * LT_ERR_NO_MEMORY instead of allocating.  Replays of graphs captured on one
+ * stream share that stream's buffer with each other and with eager calls, so
+ * they must not run concurrently (stream order serialises them).
  * Returns LT_OK, LT_ERR_INVALID_ARG, LT_ERR_NO_MEMORY or LT_ERR_HIP.
- * Synchronises `stream` when it has to grow the buffer.
  */
 LT_API int lt_reserve(int64_t max_T, int64_t L, void *stream);
 
-/* Free every scratch buffer of the current device (synchronises the device). */
+/*
+ * lt_release_scratch -- synchronise the current device and free every scratch
+ * buffer the library holds on it (current and replaced ones).  Every graph
+ * that captured a call of the large-token path on this device becomes
+ * invalid: replaying it afterwards is an error of the caller.  Needed only to
+ * return the memory before process exit.  The lifetime rule exists for the
+ * graph replay of [PR50593 Implementation, item 4].
+ */
 LT_API int lt_release_scratch(void);
 
 /*
@@ -169,29 +197,37 @@ LT_API int lt_release_scratch(void);
  */
 LT_API int64_t lt_set_skinny_max_tokens(int64_t t);
 
-/* Current threshold (see lt_set_skinny_max_tokens). */
+/* Current threshold (see lt_set_skinny_max_tokens; [PR50383 Implementation,
+ * item 1]). */
 LT_API int64_t lt_get_skinny_max_tokens(void);
 
 /*
  * lt_path_for -- which path a call with these sizes takes:
- * 0 = nothing launched (T == 0 or n == 0), 1 = weight-streaming (skinny),
- * 2 = sum+RMSNorm kernel then MFMA GEMM (the GEMM alone for one partial with
- * norm_w == NULL).  Host-only, launches nothing.
+ * 0 = nothing launched (T == 0 or n == 0; [PR50383 Key source snippets,
+ * `_select_tail_tier`] treats a positive token count as the precondition of
+ * every tier), 1 = weight-streaming (skinny), 2 = sum+RMSNorm kernel then
+ * MFMA GEMM (the GEMM alone for one partial with norm_w == NULL).  The
+ * tier is a function of the token count alone, as there.  Host-only,
+ * launches nothing.
  */
 LT_API int lt_path_for(int64_t T, int64_t n);
 
 /*
- * lt_set_kernel_events -- timing hook for benchmarks and profilers.  While set
- * (non-NULL), every lt_latent_tail call records the hipEvent_t `before` on its
- * stream immediately before launching its projection kernel (k_skinny, or
- * k_gemm on the large-token path) and `after` immediately after it, so the
- * caller can time that kernel alone with hipEventElapsedTime.  Pass NULL, NULL
- * to switch it off (the default).  Process-wide; not for concurrent callers.
+ * lt_set_kernel_events -- per-kernel timing hook, the measurement that an
+ * operator benchmark takes ([PR50593 Implementation, item 4] reports operator
+ * latencies on gfx950).  While set (non-NULL) for the calling thread, every
+ * lt_latent_tail / lt_latent_tail_residual call made from that thread records
+ * the hipEvent_t `before` on its stream immediately before launching its
+ * projection kernel (k_skinny, or the GEMM on the large-token path) and
+ * `after` immediately after it, so the caller can time that kernel alone with
+ * hipEventElapsedTime.  Pass NULL, NULL to switch it off (the default).
+ * The setting is per host thread; calls from other threads are unaffected.
  * Returns LT_OK.
  */
 LT_API int lt_set_kernel_events(void *before, void *after);
 
-/* Library version string, e.g. "liblatenttail 0.1.0 gfx950". */
+/* Library version string, e.g. "liblatenttail 0.2.0 gfx950".  No passage
+ * defines it; it names the build in logs. */
 LT_API const char *lt_version(void);
 
 #ifdef __cplusplus

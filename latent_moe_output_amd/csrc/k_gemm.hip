@@ -53,6 +53,7 @@
 
 #include "lt_device.h"
 #include "lt_internal.h"
+#include "lt_launch.h"
 
 namespace lt {
 namespace {
@@ -908,23 +909,22 @@ hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16
     const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
     const bool kt = L % BK != 0;
 #define LT_RING(NKR, KT, R)                                                                  \
-    hipLaunchKernelGGL((k_gemm_ring<BJ, WGJ, WGT, GROUP_J, NKR, KT, R>), grid, block, 0, stream, \
-                       y, ntj, (int)ntt, T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
+    launch(&k_gemm_ring<BJ, WGJ, WGT, GROUP_J, NKR, KT, R>, grid, block, stream, y, ntj, (int)ntt, \
+           T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
 #define LT_RING_K(NKR)                                                                       \
-    do {                                                                                     \
-        if (kt) { if (res) LT_RING(NKR, true, true); else LT_RING(NKR, true, false); }       \
-        else { if (res) LT_RING(NKR, false, true); else LT_RING(NKR, false, false); }        \
-    } while (0)
+    (kt ? (res ? LT_RING(NKR, true, true) : LT_RING(NKR, true, false))                      \
+        : (res ? LT_RING(NKR, false, true) : LT_RING(NKR, false, false)))
+    hipError_t e;
     switch (nk % 5) {
-    case 0: LT_RING_K(0); break;
-    case 1: LT_RING_K(1); break;
-    case 2: LT_RING_K(2); break;
-    case 3: LT_RING_K(3); break;
-    default: LT_RING_K(4); break;
+    case 0: e = LT_RING_K(0); break;
+    case 1: e = LT_RING_K(1); break;
+    case 2: e = LT_RING_K(2); break;
+    case 3: e = LT_RING_K(3); break;
+    default: e = LT_RING_K(4); break;
     }
 #undef LT_RING_K
 #undef LT_RING
-    return hipGetLastError();
+    return e;
 }
 
 template <int BJ, int BT, int WGJ, int WGT, int NS, int GROUP_J>
@@ -947,23 +947,17 @@ hipError_t launch_cfg(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 
     u16 *rsd = res ? res->resid : nullptr;
     const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
 #define LT_GEMM_LAUNCH(KT, EPI, R)                                                           \
-    hipLaunchKernelGGL((k_gemm<BJ, BT, WGJ, WGT, NS, GROUP_J, KT, EPI, R>), grid, block, 0, stream, \
-                       y, ntj, (int)ntt, T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
+    launch(&k_gemm<BJ, BT, WGJ, WGT, NS, GROUP_J, KT, EPI, R>, grid, block, stream, y, ntj,         \
+           (int)ntt, T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
 #define LT_GEMM_LAUNCH_R(KT, EPI)                                                            \
-    do {                                                                                     \
-        if (res) LT_GEMM_LAUNCH(KT, EPI, true); else LT_GEMM_LAUNCH(KT, EPI, false);        \
-    } while (0)
+    (res ? LT_GEMM_LAUNCH(KT, EPI, true) : LT_GEMM_LAUNCH(KT, EPI, false))
     const bool kt = L % (NS * BK) != 0;
     if constexpr (EPI_OK) {
-        if (epi) {
-            if (kt) LT_GEMM_LAUNCH_R(true, true); else LT_GEMM_LAUNCH_R(false, true);
-            return hipGetLastError();
-        }
+        if (epi) return kt ? LT_GEMM_LAUNCH_R(true, true) : LT_GEMM_LAUNCH_R(false, true);
     }
-    if (kt) LT_GEMM_LAUNCH_R(true, false); else LT_GEMM_LAUNCH_R(false, false);
+    return kt ? LT_GEMM_LAUNCH_R(true, false) : LT_GEMM_LAUNCH_R(false, false);
 #undef LT_GEMM_LAUNCH_R
 #undef LT_GEMM_LAUNCH
-    return hipGetLastError();
 }
 
 }  // namespace

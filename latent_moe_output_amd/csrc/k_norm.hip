@@ -13,6 +13,7 @@
 // lt_latent.h, so loads and stores cover whole 128-byte lines.
 #include "lt_internal.h"
 #include "lt_latent.h"
+#include "lt_launch.h"
 
 namespace lt {
 namespace {
@@ -108,12 +109,10 @@ hipError_t launch_ni(const u16 *part, int64_t pstride, int P, int64_t T, int L,
 {
     const dim3 grid((unsigned)((T + 15) / 16)), block(64 * KW);
     if (P == 1)
-        hipLaunchKernelGGL((k_sum_rmsnorm<NI, true>), grid, block, 0, stream, part, pstride, P, T,
-                           L, norm_w, eps, 1.0f / (float)L, y);
-    else
-        hipLaunchKernelGGL((k_sum_rmsnorm<NI, false>), grid, block, 0, stream, part, pstride, P, T,
-                           L, norm_w, eps, 1.0f / (float)L, y);
-    return hipGetLastError();
+        return launch(&k_sum_rmsnorm<NI, true>, grid, block, stream, part, pstride, P, T, L, norm_w,
+                      eps, 1.0f / (float)L, y);
+    return launch(&k_sum_rmsnorm<NI, false>, grid, block, stream, part, pstride, P, T, L, norm_w,
+                  eps, 1.0f / (float)L, y);
 }
 
 }  // namespace
@@ -122,9 +121,8 @@ hipError_t launch_sum_partials(const uint16_t *part, int64_t pstride, int P, int
                                uint16_t *s, hipStream_t stream)
 {
     const int64_t threads = (count + 7) / 8;
-    hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, part, pstride, P, count, s);
-    return hipGetLastError();
+    return launch(&k_sum_partials, dim3((unsigned)((threads + 255) / 256)), dim3(256), stream, part,
+                  pstride, P, count, s);
 }
 
 hipError_t launch_sum_rmsnorm(const uint16_t *part, int64_t pstride, int P, int64_t T, int L,

@@ -52,6 +52,7 @@
 // n, so column shards reproduce the full-window result bit for bit.
 #include "lt_internal.h"
 #include "lt_latent.h"
+#include "lt_launch.h"
 
 namespace lt {
 namespace {
@@ -259,17 +260,14 @@ hipError_t launch_nt(const u16 *part, int64_t pstride, int P, int T, int L, cons
     // W rows through LDS while the staged latent and W fit in it
     constexpr bool WS = NI <= 4;
 #define LT_SKINNY_LAUNCH(R, S)                                                                  \
-    hipLaunchKernelGGL((k_skinny<NI, TT, JT, R, S, WS>), grid, block, 0, stream, part, Wn, outn,   \
-                       norm_w, ld_out, T, L, n, RW | (vec8 << 8), pstride, P, eps, 1.0f / (float)L,  \
-                       pre, ldp, rsd, ldr)
+    launch(&k_skinny<NI, TT, JT, R, S, WS>, grid, block, stream, part, Wn, outn, norm_w, ld_out, T,  \
+           L, n, RW | (vec8 << 8), pstride, P, eps, 1.0f / (float)L, pre, ldp, rsd, ldr)
     // one partial: the latent tiles are staged through LDS as whole lines
-    if (res) {
-        if (P == 1) LT_SKINNY_LAUNCH(true, true); else LT_SKINNY_LAUNCH(true, false);
-    } else {
-        if (P == 1) LT_SKINNY_LAUNCH(false, true); else LT_SKINNY_LAUNCH(false, false);
-    }
+    hipError_t e;
+    if (res) e = P == 1 ? LT_SKINNY_LAUNCH(true, true) : LT_SKINNY_LAUNCH(true, false);
+    else e = P == 1 ? LT_SKINNY_LAUNCH(false, true) : LT_SKINNY_LAUNCH(false, false);
 #undef LT_SKINNY_LAUNCH
-    return hipGetLastError();
+    return e;
 }
 
 template <int NI, int JT>

@@ -24,7 +24,10 @@
 #include <cstdlib>
 #include <map>
 #include <mutex>
+#include <thread>
+#include <tuple>
 #include <utility>
+#include <vector>
 
 #include "latent_tail.h"
 #include "lt_internal.h"
@@ -39,13 +42,13 @@ constexpr int64_t kDefaultSkinnyMax = 64;
 constexpr int64_t kPreSumMaxT = 1024;
 
 std::atomic<int64_t> g_skinny_max{-1};
-std::atomic<void *> g_ev_before{nullptr};
-std::atomic<void *> g_ev_after{nullptr};
+// timing events of lt_set_kernel_events, per calling thread
+thread_local void *g_ev_before = nullptr;
+thread_local void *g_ev_after = nullptr;
 
-// Records the benchmark timing event `which` (if set) on `s`.
-bool record_hook(const std::atomic<void *> &which, hipStream_t s)
+// Records the timing event `ev` (if set) on `s`.
+bool record_hook(void *ev, hipStream_t s)
 {
-    void *ev = which.load(std::memory_order_relaxed);
     return !ev || hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) == hipSuccess;
 }
 
@@ -70,24 +73,46 @@ int64_t skinny_max()
 }
 
 // ---- scratch: one [T][L] bf16 latent buffer per (device, stream) ----------
+// hipStreamPerThread is one handle that names a different stream in every
+// host thread, so for it the calling thread is part of the key.
+struct ScratchKey {
+    int dev;
+    uintptr_t stream;
+    std::thread::id tid;
+    bool operator<(const ScratchKey &o) const
+    {
+        return std::tie(dev, stream, tid) < std::tie(o.dev, o.stream, o.tid);
+    }
+};
 struct Scratch {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
-// g_mu guards the map and every buffer in it: a caller holds it from looking
-// a buffer up until the kernels that use it are enqueued, so another thread
-// that grows (frees and reallocates) the same stream's buffer either runs
-// first or synchronises the stream after those kernels are in it.
+// g_mu guards the map and every buffer in it.  A caller holds it from
+// looking a buffer up until the kernels that use it are enqueued, so two
+// calls on one stream from different threads never interleave their norm
+// and GEMM kernels on one buffer.
 std::mutex g_mu;
-std::map<std::pair<int, uintptr_t>, Scratch> g_scratch;
+std::map<ScratchKey, Scratch> g_scratch;
+// Buffers that a larger one replaced.  Kernels already queued, and graphs
+// captured earlier, may still read and write them, so they stay allocated
+// until lt_release_scratch (growth neither frees nor synchronises).
+std::vector<std::pair<int, void *>> g_retired;
+
+ScratchKey scratch_key(int dev, hipStream_t stream)
+{
+    return {dev, reinterpret_cast<uintptr_t>(stream),
+            stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id()};
+}
 
 // Returns a scratch buffer of at least `bytes` for (current device, stream).
-// The caller holds g_mu.
+// The caller holds g_mu.  Sizes are powers of two from 1 MiB, so the retired
+// buffers of a stream never add up to more than its current one.
 int ensure_scratch(size_t bytes, hipStream_t stream, void **out_ptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return LT_ERR_HIP;
-    Scratch &s = g_scratch[{dev, reinterpret_cast<uintptr_t>(stream)}];
+    Scratch &s = g_scratch[scratch_key(dev, stream)];
     if (s.bytes >= bytes) {
         *out_ptr = s.ptr;
         return LT_OK;
@@ -95,19 +120,18 @@ int ensure_scratch(size_t bytes, hipStream_t stream, void **out_ptr)
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return LT_ERR_HIP;
     if (cap != hipStreamCaptureStatusNone) return LT_ERR_NO_MEMORY;  // never allocate in capture
-    // Work already queued on this stream may still read the old buffer.
-    if (s.ptr) {
-        if (hipStreamSynchronize(stream) != hipSuccess) return LT_ERR_HIP;
-        if (hipFree(s.ptr) != hipSuccess) return LT_ERR_HIP;
-        s.ptr = nullptr;
-        s.bytes = 0;
+    size_t want = (size_t)1 << 20;
+    while (want < bytes) {
+        if (want > SIZE_MAX / 2) return LT_ERR_NO_MEMORY;
+        want <<= 1;
     }
-    size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
+    const hipError_t pending = hipPeekAtLastError();
     void *p = nullptr;
     if (hipMalloc(&p, want) != hipSuccess) {
-        (void)hipGetLastError();
+        if (pending == hipSuccess) (void)hipGetLastError();   // only the error this call set
         return LT_ERR_NO_MEMORY;
     }
+    if (s.ptr) g_retired.emplace_back(dev, s.ptr);
     s.ptr = p;
     s.bytes = want;
     *out_ptr = p;
@@ -147,7 +171,7 @@ const char *lt_status_string(int status)
     }
 }
 
-const char *lt_version(void) { return "liblatenttail 0.1.0 gfx950"; }
+const char *lt_version(void) { return "liblatenttail 0.2.0 gfx950"; }
 
 int64_t lt_set_skinny_max_tokens(int64_t t)
 {
@@ -160,8 +184,8 @@ int64_t lt_get_skinny_max_tokens(void) { return skinny_max(); }
 
 int lt_set_kernel_events(void *before, void *after)
 {
-    g_ev_before.store(before, std::memory_order_relaxed);
-    g_ev_after.store(after, std::memory_order_relaxed);
+    g_ev_before = before;
+    g_ev_after = after;
     return LT_OK;
 }
 
@@ -189,9 +213,17 @@ int lt_release_scratch(void)
     std::lock_guard<std::mutex> lock(g_mu);
     if (hipDeviceSynchronize() != hipSuccess) return LT_ERR_HIP;
     for (auto it = g_scratch.begin(); it != g_scratch.end();) {
-        if (it->first.first == dev) {
+        if (it->first.dev == dev) {
             if (it->second.ptr && hipFree(it->second.ptr) != hipSuccess) return LT_ERR_HIP;
             it = g_scratch.erase(it);
+        } else {
+            ++it;
+        }
+    }
+    for (auto it = g_retired.begin(); it != g_retired.end();) {
+        if (it->first == dev) {
+            if (hipFree(it->second) != hipSuccess) return LT_ERR_HIP;
+            it = g_retired.erase(it);
         } else {
             ++it;
         }
@@ -269,7 +301,6 @@ int tail_impl(const void *partials, int n_partials, int64_t T, int64_t L, const 
     const uint16_t *Wn = static_cast<const uint16_t *>(W) + c0 * L;
     uint16_t *outn = static_cast<uint16_t *>(out) + c0;
 
-    (void)hipGetLastError();  // start from a clean error state
     if (T <= skinny_max()) {
         const int per = lt::skinny_tokens_per_launch((int)L);
         if (!record_hook(g_ev_before, s)) return LT_ERR_HIP;

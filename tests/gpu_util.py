@@ -78,14 +78,3 @@ def assert_window_close(got: np.ndarray, ref: np.ndarray, c0: int, n: int, what:
     if not np.array_equal(got[outside], ref[outside]):
         idx = np.argwhere(outside & (got != ref))[0]
         raise AssertionError("%s: element outside the window changed at %s" % (what, tuple(idx)))
-
-
-def sample_rows(T: int, k: int = 40, seed: int = 0) -> np.ndarray:
-    """Rows for sampled oracle checks: both ends, tile edges, random rows."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    rows = {0, 1, T - 1, T - 2}
-    for edge in (16, 63, 64, 65, 127, 128, 255, 256, 257, 511, 512, 4095, 4096, 8190, 8191):
-        if edge < T:
-            rows.add(edge)
-    rows.update(int(x) for x in rng.integers(0, T, size=k))
-    return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
