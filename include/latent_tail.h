@@ -49,6 +49,7 @@ extern "C" {
 #define LT_ERR_UNSUPPORTED 2   /* legal in principle, outside what this build handles */
 #define LT_ERR_NO_MEMORY 3     /* scratch could not be (re)allocated */
 #define LT_ERR_HIP 4           /* a HIP call or kernel launch failed */
+#define LT_ERR_SCRATCH_LIMIT 5 /* lt_latent_tail_noalloc: T*L beyond its fixed scratch */
 
 /* Largest latent width the kernels accept (the model's is 1024). */
 #define LT_MAX_L 2048
@@ -143,6 +144,34 @@ LT_API int lt_latent_tail_residual(const void *partials, int n_partials, int64_t
                                    int64_t c0, int64_t n, void *out, int64_t ld_out,
                                    const void *prefix, int64_t ld_prefix, void *resid,
                                    int64_t ld_resid, void *stream);
+
+/*
+ * lt_latent_tail_noalloc -- lt_latent_tail for callers that cannot allocate
+ * device memory: code being captured into a HIP graph without a prior
+ * lt_reserve, tight serving loops, and harnesses that forbid hipMalloc.
+ * Same arguments, results (bit for bit) and status codes as lt_latent_tail;
+ * it never calls hipMalloc or hipFree, nor any allocating library routine.
+ *
+ * The large-token path's [T][L] bf16 latent goes to a fixed device array of
+ * LT_NOALLOC_MAX_LATENT elements (16 MiB), one per GPU, held until the
+ * process ends.  A call that takes that path with T * L larger than
+ * LT_NOALLOC_MAX_LATENT returns LT_ERR_SCRATCH_LIMIT before anything is
+ * launched (use lt_latent_tail there).  The weight-streaming path (T <=
+ * skinny_max) and one partial with norm_w == NULL use no scratch and have
+ * no such limit.  Every element of the array that a call reads is written
+ * earlier by the same call, so no state carries over between calls.
+ *
+ * All calls on one GPU share its array: calls that may overlap on one GPU
+ * (different streams without an ordering between them, or replays of
+ * captured calls running concurrently) race on it and give wrong results.
+ * Calls on one stream are ordered and safe, from any number of threads.
+ * The first call on a device resolves the array's address on that device.
+ */
+#define LT_NOALLOC_MAX_LATENT (8u * 1024u * 1024u)
+LT_API int lt_latent_tail_noalloc(const void *partials, int n_partials, int64_t T, int64_t L,
+                                  const void *norm_w, float eps, const void *W, int64_t H,
+                                  int64_t c0, int64_t n, void *out, int64_t ld_out,
+                                  void *stream);
 
 /*
  * lt_status_string -- human-readable name of a status code (static storage,

@@ -21,6 +21,8 @@ LT_ERR_INVALID_ARG = 1
 LT_ERR_UNSUPPORTED = 2
 LT_ERR_NO_MEMORY = 3
 LT_ERR_HIP = 4
+LT_ERR_SCRATCH_LIMIT = 5
+LT_NOALLOC_MAX_LATENT = 8 * 1024 * 1024
 LT_MAX_L = 2048
 
 _lib = None
@@ -46,6 +48,9 @@ def load():
     lib.lt_latent_tail.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_float, vp, i64,
                                    i64, i64, vp, i64, vp]
     lib.lt_latent_tail.restype = ctypes.c_int
+    lib.lt_latent_tail_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_float, vp,
+                                           i64, i64, i64, vp, i64, vp]
+    lib.lt_latent_tail_noalloc.restype = ctypes.c_int
     lib.lt_latent_tail_residual.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_float, vp,
                                             i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.lt_latent_tail_residual.restype = ctypes.c_int
@@ -97,6 +102,14 @@ def lt_latent_tail(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld
     return int(load().lt_latent_tail(_ptr(partials), int(n_partials), int(T), int(L),
                                       _ptr(norm_w), float(eps), _ptr(W), int(H), int(c0),
                                       int(n), _ptr(out), int(ld_out), _stream(stream)))
+
+
+def lt_latent_tail_noalloc(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld_out,
+                           stream=None) -> int:
+    """Forward to the C entry point; returns its status code."""
+    return int(load().lt_latent_tail_noalloc(_ptr(partials), int(n_partials), int(T), int(L),
+                                              _ptr(norm_w), float(eps), _ptr(W), int(H), int(c0),
+                                              int(n), _ptr(out), int(ld_out), _stream(stream)))
 
 
 def lt_latent_tail_residual(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld_out,

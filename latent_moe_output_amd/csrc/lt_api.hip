@@ -138,6 +138,33 @@ int ensure_scratch(size_t bytes, hipStream_t stream, void **out_ptr)
     return LT_OK;
 }
 
+// ---- the fixed scratch of lt_latent_tail_noalloc ---------------------------
+// One [T][L] bf16 latent of at most LT_NOALLOC_MAX_LATENT elements per
+// device, held for the life of the process.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the device address that
+// hipGetSymbolAddress returns for the current device (g_noalloc_ptr), never
+// the array's name.  Every noalloc call on a device shares its array.
+static __device__ __align__(256) uint16_t scratch[LT_NOALLOC_MAX_LATENT];
+
+constexpr int kMaxDevices = 64;
+void *g_noalloc_ptr[kMaxDevices] = {};   // guarded by g_mu
+
+// Device address of the current device's `scratch`, resolved once per
+// device (no allocation).  The caller holds g_mu.
+int noalloc_scratch(void **out_ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LT_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return LT_ERR_UNSUPPORTED;
+    if (!g_noalloc_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LT_ERR_HIP;
+        g_noalloc_ptr[dev] = p;
+    }
+    *out_ptr = g_noalloc_ptr[dev];
+    return LT_OK;
+}
+
 bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb)
 {
     if (!a || !b || na == 0 || nb == 0) return false;
@@ -167,6 +194,8 @@ const char *lt_status_string(int status)
     case LT_ERR_UNSUPPORTED: return "LT_ERR_UNSUPPORTED: latent width or alignment not handled";
     case LT_ERR_NO_MEMORY: return "LT_ERR_NO_MEMORY: scratch could not be allocated";
     case LT_ERR_HIP: return "LT_ERR_HIP: HIP call or kernel launch failed";
+    case LT_ERR_SCRATCH_LIMIT:
+        return "LT_ERR_SCRATCH_LIMIT: T*L exceeds the fixed scratch of lt_latent_tail_noalloc";
     default: return "unknown lt status";
     }
 }
@@ -236,10 +265,12 @@ int lt_release_scratch(void)
 namespace {
 
 // The tail, with the residual update when `res` is set (its pointers
-// validated by the caller and not yet offset by c0).
+// validated by the caller and not yet offset by c0).  With `fixed` the
+// large-token path's latent goes to the device's fixed `scratch` array
+// (nothing is allocated); otherwise to the stream's growable buffer.
 int tail_impl(const void *partials, int n_partials, int64_t T, int64_t L, const void *norm_w,
               float eps, const void *W, int64_t H, int64_t c0, int64_t n, void *out,
-              int64_t ld_out, const lt::Resid *res_in, void *stream)
+              int64_t ld_out, const lt::Resid *res_in, void *stream, bool fixed)
 {
     // ---- sizes and window
     if (n_partials < 1 || T < 0 || L < 1 || H < 1 || c0 < 0 || n < 0 || c0 > H || n > H - c0 ||
@@ -327,12 +358,13 @@ int tail_impl(const void *partials, int n_partials, int64_t T, int64_t L, const 
         return record_hook(g_ev_after, s) ? LT_OK : LT_ERR_HIP;
     }
 
+    if (fixed && tl > (int64_t)LT_NOALLOC_MAX_LATENT) return LT_ERR_SCRATCH_LIMIT;
     // the scratch stays locked until both kernels that use it are enqueued
     std::lock_guard<std::mutex> lock(g_mu);
-    void *scratch = nullptr;
-    int st = ensure_scratch((size_t)tl * 2, s, &scratch);
+    void *buf = nullptr;
+    int st = fixed ? noalloc_scratch(&buf) : ensure_scratch((size_t)tl * 2, s, &buf);
     if (st != LT_OK) return st;
-    uint16_t *y = static_cast<uint16_t *>(scratch);
+    uint16_t *y = static_cast<uint16_t *>(buf);
     if (n_partials > 1 && T < kPreSumMaxT) {
         // Few 16-token tiles: the sum+RMSNorm kernel would pull every
         // partial of a tile through one CU.  The partials are summed first
@@ -361,7 +393,15 @@ int lt_latent_tail(const void *partials, int n_partials, int64_t T, int64_t L,
                    int64_t n, void *out, int64_t ld_out, void *stream)
 {
     return tail_impl(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld_out, nullptr,
-                     stream);
+                     stream, false);
+}
+
+int lt_latent_tail_noalloc(const void *partials, int n_partials, int64_t T, int64_t L,
+                           const void *norm_w, float eps, const void *W, int64_t H, int64_t c0,
+                           int64_t n, void *out, int64_t ld_out, void *stream)
+{
+    return tail_impl(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld_out, nullptr,
+                     stream, true);
 }
 
 int lt_latent_tail_residual(const void *partials, int n_partials, int64_t T, int64_t L,
@@ -372,7 +412,7 @@ int lt_latent_tail_residual(const void *partials, int n_partials, int64_t T, int
     const lt::Resid r{static_cast<const uint16_t *>(prefix), ld_prefix,
                       static_cast<uint16_t *>(resid), ld_resid};
     return tail_impl(partials, n_partials, T, L, norm_w, eps, W, H, c0, n, out, ld_out, &r,
-                     stream);
+                     stream, false);
 }
 
 }  // extern "C"

@@ -52,7 +52,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_version_and_status_strings(lib):
     assert "gfx950" in binding.lt_version()
-    for code in range(5):
+    for code in range(6):
         assert binding.lt_status_string(code).startswith("LT_")
     assert binding.lt_status_string(99) == "unknown lt status"
 
@@ -151,3 +151,16 @@ def test_residual_invalid_arguments_are_rejected(lib, kw, code):
 def test_residual_empty_calls_launch_nothing(lib):
     assert binding.lt_latent_tail_residual(**dict(_RES_BASE, T=0)) == binding.LT_OK
     assert binding.lt_latent_tail_residual(**dict(_RES_BASE, n=0)) == binding.LT_OK
+
+
+def test_noalloc_entry_point_validates_like_the_tail(lib):
+    """lt_latent_tail_noalloc shares the tail's argument checks (all before
+    any launch); empty calls return LT_OK."""
+    args = dict(partials=FAKE, n_partials=1, T=16, L=1024, norm_w=FAKE + (1 << 30), eps=1e-6,
+                W=FAKE + (1 << 20), H=7168, c0=0, n=7168, out=FAKE + (1 << 31), ld_out=7168)
+    for kw, code in ((dict(n_partials=0), binding.LT_ERR_INVALID_ARG),
+                     (dict(eps=-1.0), binding.LT_ERR_INVALID_ARG),
+                     (dict(L=1020), binding.LT_ERR_UNSUPPORTED),
+                     (dict(out=FAKE), binding.LT_ERR_INVALID_ARG),
+                     (dict(T=0), binding.LT_OK), (dict(n=0), binding.LT_OK)):
+        assert binding.lt_latent_tail_noalloc(**dict(args, **kw)) == code, kw
