@@ -233,3 +233,62 @@ int lto_latent_tail_residual(const uint16_t *partials, int P, int64_t T, int64_t
     }
     return 0;
 }
+
+/*
+ * AttnRes state update and output norm, zero-block path.
+ *
+ * [PR50593 Implementation, item 1]: the fused AttnRes kernel loads the prefix
+ * sum and the delta, adds them in high precision, rounds the sum to bf16
+ * storage precision and uses that value from then on as the residual source
+ * (the prefix is updated in place); with a block-write index the same value
+ * lands in that slot of the block residual; the output RMSNorm keeps its
+ * variance out of bf16.  With no valid blocks the softmax over sources has
+ * the prefix as its only source, so the aggregated value is the prefix
+ * itself.  [PR50593 Key source snippets, `forward_attn_residual`]: the delta
+ * stands for the unfused `prefix_sum + hidden_states` (a bf16 add).
+ *
+ *   p'[t,h] = bf16(prefix[t,h] + delta[t,h])       (delta != NULL; else prefix)
+ *   prefix[t,h] <- p'[t,h]                          (delta != NULL)
+ *   block[t, idx, h] <- p'[t,h]                     (idx >= 0)
+ *   out[t,h] = bf16(p'[t,h] * r_t * w[h]),  r_t = 1/sqrt((1/H) sum_h p'^2 + eps)
+ *                                                   (norm_w != NULL; else p')
+ *
+ * prefix, delta, out: [T][H]; block: [T][num_slots][H]; norm_w: [H]; all
+ * bf16 bits, packed.  Every other element is left untouched.
+ * Returns 0, or -1 on bad arguments.
+ */
+int lto_attn_res_zero_block(uint16_t *prefix, const uint16_t *delta, int64_t T, int64_t H,
+                            uint16_t *block, int64_t num_slots, int64_t block_idx,
+                            const uint16_t *norm_w, double eps, uint16_t *out)
+{
+    if (T < 0 || H < 1 || num_slots < 0 || block_idx >= num_slots) return -1;
+    if (T == 0) return 0;
+    if (!prefix || !out || (block_idx >= 0 && !block)) return -1;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double *p = (double *)malloc((size_t)H * sizeof(double));
+        /* the updated prefix: one rounding of the exact sum */
+        for (int64_t h = 0; h < H; ++h) {
+            double v = lto_bf16_to_f64(prefix[t * H + h]);
+            if (delta) v += lto_bf16_to_f64(delta[t * H + h]);
+            p[h] = rne(v);
+        }
+        if (delta)
+            for (int64_t h = 0; h < H; ++h) prefix[t * H + h] = lto_f64_to_bf16(p[h]);
+        if (block_idx >= 0)
+            for (int64_t h = 0; h < H; ++h)
+                block[(t * num_slots + block_idx) * H + h] = lto_f64_to_bf16(p[h]);
+        if (norm_w) {
+            double ss = 0.0;
+            for (int64_t h = 0; h < H; ++h) ss += p[h] * p[h];
+            double r = 1.0 / sqrt(ss / (double)H + eps);
+            for (int64_t h = 0; h < H; ++h)
+                out[t * H + h] = lto_f64_to_bf16(p[h] * r * lto_bf16_to_f64(norm_w[h]));
+        } else {
+            for (int64_t h = 0; h < H; ++h) out[t * H + h] = lto_f64_to_bf16(p[h]);
+        }
+        free(p);
+    }
+    return 0;
+}

@@ -59,6 +59,9 @@ def _load():
                                              u16p, i64, i64, i64, u16p, i64, u16p, i64, u16p,
                                              i64, ctypes.c_int]
     lib.lto_latent_tail_residual.restype = ctypes.c_int
+    lib.lto_attn_res_zero_block.argtypes = [u16p, u16p, i64, i64, u16p, i64, i64, u16p,
+                                            ctypes.c_double, u16p]
+    lib.lto_attn_res_zero_block.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -161,3 +164,33 @@ def latent_tail_residual(partials, norm_w, eps, W, c0, n, out, prefix, resid=Non
     if rc != 0:
         raise ValueError("lto_latent_tail_residual rejected its arguments")
     return o, r
+
+
+def attn_res_zero_block(prefix, delta, block, block_idx, norm_w, eps):
+    """AttnRes state update + output norm with no valid blocks.
+
+    prefix [T][H], delta [T][H] or None, block [T][S][H] or None (with
+    block_idx < 0), norm_w [H] or None; uint16 bf16 bits.  Returns copies
+    (prefix', block', out) after the update; block' is None when block is.
+    """
+    pre = np.array(_u16(prefix), copy=True)
+    if pre.ndim != 2:
+        raise ValueError("prefix must be [T][H]")
+    T, H = pre.shape
+    dl = _u16(delta)
+    if dl is not None and dl.shape != (T, H):
+        raise ValueError("delta must be [T][H]")
+    blk = None if block is None else np.array(_u16(block), copy=True)
+    S = 0 if blk is None else blk.shape[1]
+    if blk is not None and (blk.ndim != 3 or blk.shape[0] != T or blk.shape[2] != H):
+        raise ValueError("block must be [T][S][H]")
+    w = _u16(norm_w)
+    if w is not None and w.shape != (H,):
+        raise ValueError("norm_w must have shape (H,)")
+    out = np.zeros((T, H), dtype=np.uint16)
+    rc = _load().lto_attn_res_zero_block(_ptr(pre), _ptr(dl), T, H, _ptr(blk), S,
+                                         int(block_idx), _ptr(w), float(eps), _ptr(out))
+    if rc != 0:
+        raise ValueError("lto_attn_res_zero_block rejected its arguments")
+    return pre, blk, out
+
