@@ -174,6 +174,57 @@ LT_API int lt_latent_tail_noalloc(const void *partials, int n_partials, int64_t 
                                   void *stream);
 
 /*
+ * lt_attn_res_zero_block -- the AttnRes state update and output RMSNorm of a
+ * decoder layer, for the case of no valid blocks.
+ *
+ * [PR50593 Implementation, item 1]: the fused AttnRes kernel adds the delta
+ * to the prefix sum in fp32, rounds the sum to bf16 storage precision and
+ * uses it as the residual source from then on (the prefix is updated in
+ * place), writes it to the block-residual slot of a block-write layer, and
+ * applies the output RMSNorm with its variance in fp32; with zero blocks the
+ * softmax has one source and the aggregated value equals the prefix.
+ * [PR50593 Key source snippets, `forward_attn_residual`]: the delta stands
+ * for the unfused `prefix_sum + hidden_states`.  For t < T, h < H:
+ *
+ *   p'[t][h]  = bf16( prefix[t][h] + delta[t][h] )   (= prefix if delta NULL)
+ *   prefix[t][h] = p'[t][h]                           (only when delta != NULL)
+ *   block_residual[t][block_idx][h] = p'[t][h]         (only when block_idx >= 0)
+ *   out[t][h] = bf16( p'[t][h] * rsqrt(mean_h p'[t][.]^2 + eps) * norm_w[h] )
+ *               (fp32 variance and scaling; out = p' when norm_w == NULL)
+ *
+ * The softmax aggregation over one or more valid blocks (the layer's
+ * res_proj and res_norm) is not part of this call.
+ *
+ * Arguments (all bf16 bit patterns, device pointers, packed row-major,
+ * 16-byte aligned):
+ *   prefix          [T][H], read; updated in place when delta != NULL.
+ *   delta           [T][H] or NULL (the pages' HAS_DELTA switch).
+ *   T               tokens, >= 0.
+ *   H               hidden width, H % 8 == 0, 8 <= H <= LT_ATTN_RES_MAX_H.
+ *   block_residual  [T][num_slots][H]; only slot block_idx of each token is
+ *                   written, every other element is left bit-identical.
+ *                   May be NULL when block_idx == -1.
+ *   num_slots       slots per token of block_residual, >= 0.
+ *   block_idx       slot to write, -1 for none (the pages' WRITE_BLOCK
+ *                   switch), < num_slots.
+ *   norm_w          [H] output-norm weight, or NULL (APPLY_OUTPUT_NORM).
+ *   eps             >= 0 and finite; added to the mean square inside the root.
+ *   out             [T][H], written.
+ *   stream          hipStream_t (NULL = default stream).
+ * out must not overlap any other buffer; block_residual must not overlap
+ * prefix, delta or norm_w; prefix must not overlap delta or norm_w.
+ *
+ * Returns LT_OK, LT_ERR_INVALID_ARG (range, NULL or overlap), LT_ERR_UNSUPPORTED
+ * (H not a multiple of 8 or above LT_ATTN_RES_MAX_H, a misaligned pointer,
+ * T above 2^31 - 1) or LT_ERR_HIP; errors are returned before any launch.
+ * T == 0 returns LT_OK with nothing launched.
+ */
+#define LT_ATTN_RES_MAX_H 8192
+LT_API int lt_attn_res_zero_block(void *prefix, const void *delta, int64_t T, int64_t H,
+                                  void *block_residual, int64_t num_slots, int64_t block_idx,
+                                  const void *norm_w, float eps, void *out, void *stream);
+
+/*
  * lt_status_string -- human-readable name of a status code (static storage,
  * never NULL).  The pages' runner falls back silently, with one warning, when
  * a precondition of the sharded tail fails ([PR51253 Implementation, item 2];

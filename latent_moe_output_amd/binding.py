@@ -23,6 +23,7 @@ LT_ERR_NO_MEMORY = 3
 LT_ERR_HIP = 4
 LT_ERR_SCRATCH_LIMIT = 5
 LT_NOALLOC_MAX_LATENT = 8 * 1024 * 1024
+LT_ATTN_RES_MAX_H = 8192
 LT_MAX_L = 2048
 
 _lib = None
@@ -54,6 +55,9 @@ def load():
     lib.lt_latent_tail_residual.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.c_float, vp,
                                             i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.lt_latent_tail_residual.restype = ctypes.c_int
+    lib.lt_attn_res_zero_block.argtypes = [vp, vp, i64, i64, vp, i64, i64, vp, ctypes.c_float,
+                                           vp, vp]
+    lib.lt_attn_res_zero_block.restype = ctypes.c_int
     lib.lt_status_string.argtypes = [ctypes.c_int]
     lib.lt_status_string.restype = ctypes.c_char_p
     lib.lt_reserve.argtypes = [i64, i64, vp]
@@ -119,6 +123,15 @@ def lt_latent_tail_residual(partials, n_partials, T, L, norm_w, eps, W, H, c0, n
         _ptr(partials), int(n_partials), int(T), int(L), _ptr(norm_w), float(eps), _ptr(W),
         int(H), int(c0), int(n), _ptr(out), int(ld_out), _ptr(prefix), int(ld_prefix),
         _ptr(resid), int(ld_resid), _stream(stream)))
+
+
+def lt_attn_res_zero_block(prefix, delta, T, H, block_residual, num_slots, block_idx, norm_w,
+                           eps, out, stream=None) -> int:
+    """Forward to the C entry point; returns its status code."""
+    return int(load().lt_attn_res_zero_block(_ptr(prefix), _ptr(delta), int(T), int(H),
+                                              _ptr(block_residual), int(num_slots),
+                                              int(block_idx), _ptr(norm_w), float(eps),
+                                              _ptr(out), _stream(stream)))
 
 
 def lt_status_string(status: int) -> str:

@@ -415,4 +415,42 @@ int lt_latent_tail_residual(const void *partials, int n_partials, int64_t T, int
                      stream, false);
 }
 
+int lt_attn_res_zero_block(void *prefix, const void *delta, int64_t T, int64_t H,
+                           void *block_residual, int64_t num_slots, int64_t block_idx,
+                           const void *norm_w, float eps, void *out, void *stream)
+{
+    if (T < 0 || H < 1 || num_slots < 0 || block_idx >= num_slots || block_idx < -1)
+        return LT_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.f) return LT_ERR_INVALID_ARG;
+    if (H % 8 != 0 || H > LT_ATTN_RES_MAX_H) return LT_ERR_UNSUPPORTED;
+    if (T == 0) return LT_OK;
+    if (T > 0x7FFFFFFF) return LT_ERR_UNSUPPORTED;
+    const bool write_block = block_idx >= 0;
+    if (!prefix || !out || (write_block && !block_residual)) return LT_ERR_INVALID_ARG;
+    int64_t th = 0, tsh = 0;
+    if (!mul_ok(T, H, &th) || th > INT64_MAX / 4 || !mul_ok(th, num_slots, &tsh) ||
+        tsh > INT64_MAX / 4)
+        return LT_ERR_INVALID_ARG;
+    if (!aligned(prefix, 16) || !aligned(out, 16) || (delta && !aligned(delta, 16)) ||
+        (norm_w && !aligned(norm_w, 16)) || (write_block && !aligned(block_residual, 16)))
+        return LT_ERR_UNSUPPORTED;
+    // out and the block are written, the prefix too when there is a delta:
+    // none of them may overlap another buffer
+    const size_t rb = (size_t)th * 2, bb = (size_t)tsh * 2, wb = (size_t)H * 2;
+    const void *blk = write_block ? block_residual : nullptr;
+    if (ranges_overlap(out, rb, prefix, rb) || ranges_overlap(out, rb, delta, rb) ||
+        ranges_overlap(out, rb, norm_w, wb) || ranges_overlap(out, rb, blk, bb) ||
+        ranges_overlap(blk, bb, prefix, rb) || ranges_overlap(blk, bb, delta, rb) ||
+        ranges_overlap(blk, bb, norm_w, wb) || ranges_overlap(prefix, rb, delta, rb) ||
+        ranges_overlap(prefix, rb, norm_w, wb))
+        return LT_ERR_INVALID_ARG;
+    uint16_t *slot = write_block ? static_cast<uint16_t *>(block_residual) + block_idx * H
+                                 : nullptr;
+    const hipError_t e = lt::launch_attn_res(
+        static_cast<uint16_t *>(prefix), static_cast<const uint16_t *>(delta), T, (int)H, slot,
+        num_slots * H, static_cast<const uint16_t *>(norm_w), eps, static_cast<uint16_t *>(out),
+        reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LT_OK : LT_ERR_HIP;
+}
+
 }  // extern "C"

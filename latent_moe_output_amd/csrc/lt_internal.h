@@ -46,4 +46,13 @@ hipError_t launch_sum_rmsnorm(const uint16_t *part, int64_t pstride, int P, int6
 hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
                        uint16_t *outn, int64_t ld_out, const Resid *res, hipStream_t stream);
 
+// AttnRes zero-block path: per token row t < T of width H (H % 8 == 0,
+// H <= 8192, rows 16-byte aligned), p' = bf16(prefix + delta) (delta may be
+// NULL), written back to prefix when delta is set and to block_slot +
+// t * block_stride when block_slot is set; out = bf16(p' * rsqrt(mean p'^2 +
+// eps) * w) when norm_w is set, else p'.
+hipError_t launch_attn_res(uint16_t *prefix, const uint16_t *delta, int64_t T, int H,
+                           uint16_t *block_slot, int64_t block_stride, const uint16_t *norm_w,
+                           float eps, uint16_t *out, hipStream_t stream);
+
 }  // namespace lt

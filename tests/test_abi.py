@@ -164,3 +164,44 @@ def test_noalloc_entry_point_validates_like_the_tail(lib):
                      (dict(out=FAKE), binding.LT_ERR_INVALID_ARG),
                      (dict(T=0), binding.LT_OK), (dict(n=0), binding.LT_OK)):
         assert binding.lt_latent_tail_noalloc(**dict(args, **kw)) == code, kw
+
+
+_AR = dict(prefix=FAKE, delta=FAKE + (1 << 24), T=4, H=1024, block_residual=FAKE + (1 << 25),
+           num_slots=3, block_idx=1, norm_w=FAKE + (1 << 26), eps=1e-6, out=FAKE + (1 << 27))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), binding.LT_ERR_INVALID_ARG),
+    (dict(H=0), binding.LT_ERR_INVALID_ARG),
+    (dict(block_idx=3), binding.LT_ERR_INVALID_ARG),
+    (dict(block_idx=-2), binding.LT_ERR_INVALID_ARG),
+    (dict(num_slots=-1, block_idx=-1), binding.LT_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), binding.LT_ERR_INVALID_ARG),
+    (dict(eps=-1.0), binding.LT_ERR_INVALID_ARG),
+    (dict(prefix=None), binding.LT_ERR_INVALID_ARG),
+    (dict(out=None), binding.LT_ERR_INVALID_ARG),
+    (dict(block_residual=None), binding.LT_ERR_INVALID_ARG),
+    (dict(H=1020), binding.LT_ERR_UNSUPPORTED),
+    (dict(H=8200), binding.LT_ERR_UNSUPPORTED),
+    (dict(prefix=FAKE + 8), binding.LT_ERR_UNSUPPORTED),
+    (dict(delta=FAKE + (1 << 24) + 2), binding.LT_ERR_UNSUPPORTED),
+    (dict(norm_w=FAKE + (1 << 26) + 4), binding.LT_ERR_UNSUPPORTED),
+    (dict(out=FAKE + (1 << 27) + 8), binding.LT_ERR_UNSUPPORTED),
+    (dict(block_residual=FAKE + (1 << 25) + 8), binding.LT_ERR_UNSUPPORTED),
+    (dict(out=FAKE), binding.LT_ERR_INVALID_ARG),                     # out is prefix
+    (dict(out=FAKE + (1 << 25) + 2048), binding.LT_ERR_INVALID_ARG),  # out inside the block
+    (dict(block_residual=FAKE + (1 << 24)), binding.LT_ERR_INVALID_ARG),  # block is delta
+    (dict(delta=FAKE + 4096), binding.LT_ERR_INVALID_ARG),            # delta inside prefix
+    (dict(norm_w=FAKE + 1024), binding.LT_ERR_INVALID_ARG),           # weight inside prefix
+    (dict(T=0), binding.LT_OK),
+    (dict(T=0, prefix=None, out=None), binding.LT_OK),
+])
+def test_attn_res_arguments_are_checked_before_launch(lib, kw, code):
+    assert binding.lt_attn_res_zero_block(**dict(_AR, **kw)) == code
+
+
+def test_attn_res_optional_buffers_may_be_null(lib):
+    """No delta, no block write, no norm: only prefix and out are needed (T
+    = 0, so nothing launches)."""
+    assert binding.lt_attn_res_zero_block(FAKE, None, 0, 1024, None, 0, -1, None, 0.0,
+                                          FAKE + (1 << 27)) == binding.LT_OK
