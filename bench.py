@@ -253,72 +253,189 @@ def residual_pass(binding, hip, stream, sh, sets, wpool, norm_w, call_kern, reps
 CONFIG_RUNS = ("shard", "ragged", "ragged_nonorm")
 
 
-def configs_pass(binding, hip, stream, sh, wpool, reps=10):
-    """The column-shard workloads at their real shapes (not part of `value`):
-    the 8-partial shard (T=256, window of 896 columns) and the ragged prefill
-    shard (T=8191, 4 partials, window of 896 columns) with and without the
-    norm.  Inputs drawn on the device (same distributions as the host
-    generator; the ragged workload's +-1e4 outliers are left out, they do not
-    change the work).  Each call reads its own W copy and rotates its
-    partials/out sets; back-to-back time per call from a replayed graph."""
+def tail_workload(name):
+    """A workload of synth.WORKLOADS by name; `decodeN` is the decode shape at
+    T = N."""
+    from latent_moe_output_amd import synth
+
+    if name.startswith("decode") and name[6:].isdigit():
+        return synth.WORKLOADS["decode"].with_T(int(name[6:]))
+    return synth.WORKLOADS[name]
+
+
+def time_workload(binding, hip, stream, sh, wl, wpool, reps=10):
+    """One tail workload at its real shape: inputs drawn on the device (same
+    distributions as the host generator; the ragged workload's +-1e4 outliers
+    are left out, they do not change the work), each call on its own W copy
+    and a rotated partials/out set, R calls captured into one graph and
+    replayed `reps` times; back-to-back time per call."""
     import torch
 
     from latent_moe_output_amd import synth
 
-    res = {}
-    for name in CONFIG_RUNS:
-        wl = synth.WORKLOADS[name]
-        per = 2 * wl.P * wl.T * wl.L + 2 * wl.T * wl.ld_out
-        R = int(min(16, max(2, math.ceil(ROTATE_BYTES / per))))
-        with torch.cuda.stream(stream):
-            sets = [synth.generate_device(wl, seed=s) for s in range(R)]
-        torch.cuda.synchronize()
-        nw = sets[0]["norm_w"]
+    per = 2 * wl.P * wl.T * wl.L + 2 * wl.T * wl.ld_out
+    R = int(min(16, max(2, math.ceil(ROTATE_BYTES / per))))
+    with torch.cuda.stream(stream):
+        sets = [synth.generate_device(wl, seed=s) for s in range(R)]
+    torch.cuda.synchronize()
+    nw = sets[0]["norm_w"]
+    binding.check(binding.lt_reserve(wl.T, wl.L, sh))
 
-        def one(i):
-            d = sets[i % R]
-            return binding.lt_latent_tail(d["partials"], wl.P, wl.T, wl.L, nw, wl.eps,
-                                          wpool[(5 * i) % len(wpool)], wl.H, wl.c0, wl.n,
-                                          d["out"], wl.ld_out, sh)
+    def one(i):
+        d = sets[i % R]
+        return binding.lt_latent_tail(d["partials"], wl.P, wl.T, wl.L, nw, wl.eps,
+                                      wpool[(5 * i) % len(wpool)], wl.H, wl.c0, wl.n,
+                                      d["out"], wl.ld_out, sh)
 
+    for i in range(R):
+        binding.check(one(i))
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
         for i in range(R):
             binding.check(one(i))
-        g = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(R):
-                binding.check(one(i))
-        with torch.cuda.stream(stream):
+    with torch.cuda.stream(stream):
+        g.replay()
+        a, b = hip.event(), hip.event()
+        hip.record(a, sh)
+        for _ in range(reps):
             g.replay()
-            a, b = hip.event(), hip.event()
-            hip.record(a, sh)
-            for _ in range(reps):
-                g.replay()
-            hip.record(b, sh)
+        hip.record(b, sh)
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(a, b) * 1e3 / (reps * R)
+    hip.destroy(a)
+    hip.destroy(b)
+    del sets, g
+    torch.cuda.synchronize()
+    f = 2 * wl.T * wl.L * wl.n
+    byt = 2 * wl.n * wl.L + 2 * wl.P * wl.T * wl.L + 4 * wl.T * wl.n + (2 * wl.L if wl.norm else 0)
+    roof_us = max(byt / HBM_PEAK, f / MFMA_BF16_PEAK) * 1e6
+    return {
+        "T": wl.T, "n_partials": wl.P, "c0": wl.c0, "n": wl.n, "ld_out": wl.ld_out,
+        "norm": wl.norm,
+        "path": ("skinny" if binding.lt_path_for(wl.T, wl.n) == 1 else
+                 ("sum+norm, gemm" if wl.norm or wl.P > 1 else "gemm")),
+        "call_us": round(us, 3),
+        "tflops": round(f / us / 1e6, 2),
+        "alg_gbps": round(byt / us / 1e3, 1),
+        "alg_bytes": byt,
+        "roofline_us": round(roof_us, 3),
+        "bound": "hbm" if byt / HBM_PEAK > f / MFMA_BF16_PEAK else "mfma",
+        "frac_of_roofline": round(roof_us / us, 3),
+        "timing": "graph of %d calls (own W copy and input set each) replayed %d times"
+                  % (R, reps),
+    }
+
+
+def configs_pass(binding, hip, stream, sh, wpool, reps=10):
+    """The column-shard workloads at their real shapes (not part of `value`):
+    the 8-partial shard (T=256, window of 896 columns) and the ragged prefill
+    shard (T=8191, 4 partials, window of 896 columns) with and without the
+    norm."""
+    return {name: time_workload(binding, hip, stream, sh, tail_workload(name), wpool, reps)
+            for name in CONFIG_RUNS}
+
+
+ATTN_RES_T = (1, 3, 7, 17, 320)
+ATTN_RES_H = 7168
+ATTN_RES_SLOTS = 9
+
+
+def attn_res_bytes(T, H=ATTN_RES_H):
+    """Algorithmic bytes of one AttnRes zero-block call with every switch on:
+    prefix and delta read, prefix, block slot and output written, the norm
+    weight read once."""
+    return 10 * T * H + 2 * H
+
+
+def time_attn_res(binding, hip, stream, sh, T, H=ATTN_RES_H, reps=20):
+    """lt_attn_res_zero_block with the delta, the block write and the output
+    norm, on rotated input sets (>= 256 MB for T >= 320), R calls captured
+    into one graph and replayed; back-to-back time per call."""
+    import torch
+
+    per = 2 * T * H * (3 + ATTN_RES_SLOTS)
+    R = int(min(64, max(2, math.ceil((256 << 20) / per))))
+    with torch.cuda.stream(stream):
+        g0 = torch.Generator(device="cuda")
+        g0.manual_seed(T)
+
+        def draw(shape, std=1.0, mean=0.0):
+            x = torch.randn(shape, generator=g0, device="cuda") * std + mean
+            return x.to(torch.bfloat16).view(torch.int16)
+
+        sets = [dict(p=draw((T, H)), d=draw((T, H), 0.1), b=draw((T, ATTN_RES_SLOTS, H)),
+                     o=torch.empty((T, H), dtype=torch.int16, device="cuda"))
+                for _ in range(R)]
+        w = draw((H,), 0.1, 1.0)
+    torch.cuda.synchronize()
+
+    def one(i):
+        d = sets[i % R]
+        return binding.lt_attn_res_zero_block(d["p"], d["d"], T, H, d["b"], ATTN_RES_SLOTS,
+                                              i % ATTN_RES_SLOTS, w, EPS, d["o"], sh)
+
+    for i in range(R):
+        binding.check(one(i))
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(R):
+            binding.check(one(i))
+    with torch.cuda.stream(stream):
+        g.replay()
+        a, b = hip.event(), hip.event()
+        hip.record(a, sh)
+        for _ in range(reps):
+            g.replay()
+        hip.record(b, sh)
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(a, b) * 1e3 / (reps * R)
+    hip.destroy(a)
+    hip.destroy(b)
+    del sets, g
+    torch.cuda.synchronize()
+    byt = attn_res_bytes(T, H)
+    return {"T": T, "H": H, "call_us": round(us, 3), "alg_bytes": byt,
+            "alg_gbps": round(byt / us / 1e3, 1), "roofline_us": round(byt / HBM_PEAK * 1e6, 3),
+            "frac_of_roofline": round(byt / HBM_PEAK / (us * 1e-6), 4), "bound": "hbm",
+            "timing": "graph of %d calls (own input set each) replayed %d times" % (R, reps)}
+
+
+def attn_res_pass(binding, hip, stream, sh):
+    """The AttnRes zero-block path at the pages' contract token counts
+    (hidden 7168, every switch on)."""
+    return {str(T): time_attn_res(binding, hip, stream, sh, T) for T in ATTN_RES_T}
+
+
+def single_workload(name, steps):
+    """Time one workload alone (for profilers): `decodeN`, `shard`, `ragged`,
+    `ragged_nonorm`, `prefill` or `attn_resN` (AttnRes zero-block path at
+    T = N, hidden 7168).  Prints one JSON line."""
+    import torch
+
+    from latent_moe_output_amd import binding
+
+    binding.load()
+    binding.lt_set_skinny_max_tokens(-1)
+    hip = Hip()
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    reps = max(1, steps)
+    if name.startswith("attn_res"):
+        res = time_attn_res(binding, hip, stream, sh, int(name[8:] or 320), reps=reps)
+    else:
+        wl = tail_workload(name)
+        nw = int(min(48, max(2, math.ceil(ROTATE_BYTES / (2 * wl.n * wl.L)))))
+        with torch.cuda.stream(stream):
+            g0 = torch.Generator(device="cuda")
+            g0.manual_seed(0)
+            W0 = (torch.randn((wl.H, wl.L), generator=g0, device="cuda") * wl.w_std).to(
+                torch.bfloat16).view(torch.int16)
+            wpool = [W0] + [W0.clone() for _ in range(nw - 1)]
         torch.cuda.synchronize()
-        us = hip.elapsed_ms(a, b) * 1e3 / (reps * R)
-        hip.destroy(a)
-        hip.destroy(b)
-        f = 2 * wl.T * wl.L * wl.n
-        byt = 2 * wl.n * wl.L + 2 * wl.P * wl.T * wl.L + 4 * wl.T * wl.n + (2 * wl.L if wl.norm else 0)
-        roof_us = max(byt / HBM_PEAK, f / MFMA_BF16_PEAK) * 1e6
-        res[name] = {
-            "T": wl.T, "n_partials": wl.P, "c0": wl.c0, "n": wl.n, "ld_out": wl.ld_out,
-            "norm": wl.norm,
-            "path": "skinny" if binding.lt_path_for(wl.T, wl.n) == 1 else "sum+norm, gemm",
-            "call_us": round(us, 3),
-            "tflops": round(f / us / 1e6, 2),
-            "alg_gbps": round(byt / us / 1e3, 1),
-            "alg_bytes": byt,
-            "roofline_us": round(roof_us, 3),
-            "bound": "hbm" if byt / HBM_PEAK > f / MFMA_BF16_PEAK else "mfma",
-            "frac_of_roofline": round(roof_us / us, 3),
-            "timing": "graph of %d calls (own W copy and input set each) replayed %d times"
-                      % (R, reps),
-        }
-        del sets, g
-        torch.cuda.synchronize()
-    return res
+        res = time_workload(binding, hip, stream, sh, wl, wpool, reps=reps)
+    print(json.dumps(dict(workload=name, **res)), flush=True)
 
 
 def cpu_baseline(d, target_s=12.0):
@@ -379,6 +496,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--workload", default=None,
+                    help="time one workload alone and exit (decodeN, shard, ragged, "
+                         "ragged_nonorm, prefill, attn_resN); for profilers")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -386,6 +506,10 @@ def main():
               "share at its real shape and nothing here talks to a second GPU "
               "(requested --gpus %d)." % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.workload:
+        single_workload(args.workload, args.steps)
+        return
 
     import numpy as np
     import torch
@@ -603,6 +727,7 @@ def main():
     }
 
     configs = configs_pass(binding, hip, stream, sh, wpool)
+    attn_res = attn_res_pass(binding, hip, stream, sh)
 
     result = {
         "metric": METRIC,
@@ -633,6 +758,7 @@ def main():
         "roofline_skinny": roofline_skinny,
         "residual": residual,
         "configs": configs,
+        "attn_res": attn_res,
         "context": context,
     }
     if not args.no_cpu:

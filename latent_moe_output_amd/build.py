@@ -38,7 +38,7 @@ def hipcc() -> str:
 COMMON = [
     "--offload-arch=" + ARCH,
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-fvisibility=hidden",
     "-DLT_BUILDING_LIBRARY",

@@ -50,6 +50,7 @@
 // Each output element's accumulation order depends on L only (K ascending in
 // 16-wide MFMA slices), not on c0, n or the tile shape.
 #include <type_traits>
+#include <utility>
 
 #include "lt_device.h"
 #include "lt_internal.h"
@@ -63,6 +64,9 @@ constexpr int ROWB = BK * 2;              // bytes per stage row (one 128-byte l
 constexpr int CPR = ROWB / 16;            // 16-byte chunks per stage row
 constexpr int KSL = BK / 16;              // 16-wide MFMA K slices per stage
 constexpr int NUM_XCD = 8;
+#ifndef LT_RING_OQ
+#define LT_RING_OQ 3   // out quarters the 256 x 256 ring fetches into registers (0, 2 or 3)
+#endif
 constexpr uint32_t OOB = LT_OOB;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
 // stores are marked non-temporal (same box, alternating runs: T = 8192 about
 // 4-8 % faster).  Same tile order, swizzles, K order and epilogue arithmetic
 // as k_gemm, so the results are bit-identical to it.
-template <int BJ, int WGJ, int WGT, int GROUP_J, int NKR, bool KTAIL, bool RES>
+template <int BJ, int WGJ, int WGT, int GROUP_J, int NKR, bool KTAIL, bool RES, int OQ>
 __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int ntj, int ntt,
                                                               int64_t T, int L, int n,
                                                               const u16 *__restrict__ Wn,
@@ -681,6 +685,31 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
         }
     };
 
+    // OQ > 0: quarters 1..OQ of the out tile are fetched into registers during
+    // the K loop, at stages nk - 8, nk - 6 and nk - 4 (one quarter per stage,
+    // QLD 16-byte loads per thread, in the order the direct loads above would
+    // write them), and written into their slots with ds_write at the end, so
+    // that the epilogue does not wait on them.  Those stages sit in a tail of
+    // the loop unrolled at compile time, so each load writes fixed registers.
+    static_assert(OQ == 0 || OQ == 2 || OQ == 3, "out quarters in registers");
+    u32x4_t oq1[QLD], oq2[QLD], oq3[QLD];
+    auto load_c_q_regs = [&](int q, u32x4_t (&rg)[QLD]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < QLD; ++it) {
+            const int idx = it * NT + 64 * w + l;
+            const int r = q * RPQ + idx / CPRE;
+            const int c = (idx % CPRE) ^ (r & (CPRE - 1));
+            rg[it] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                             rc, (uint32_t)(((int64_t)r * ld_out + j0 + 8 * c) * 2), 0, LT_NT));
+        }
+    };
+    auto store_c_q = [&](char *dst, const u32x4_t (&rg)[QLD]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < QLD; ++it)
+            *reinterpret_cast<u32x4_t *>(dst + (it * NT + 64 * w + l) * 16) = rg[it];
+    };
+
     bf16x8_t fa[2][MJ], fb[2][MT];
     auto interleave = [&](auto ND, auto NM) __attribute__((always_inline)) {
         constexpr int nd = decltype(ND)::value, nm = decltype(NM)::value;
@@ -697,19 +726,27 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
     // MODE 0: fetch B of stage k+1 and A of stage k+2 into the slots stage k-1
     // freed; 1 (stage nk-2): B of the last stage and out quarter 0; 2 (last):
     // out quarters 1 and 2.
-    auto kst = [&](auto P, auto MODE, int k) __attribute__((always_inline)) {
+    auto kst = [&](auto P, auto MODE, int k, auto QN) __attribute__((always_inline)) {
         constexpr int p = decltype(P)::value, mode = decltype(MODE)::value;
+        constexpr int qn = decltype(QN)::value;   // out quarter fetched into registers here
         using SA = I<(2 * p) % 5>;
         using SB = I<(2 * p + 1) % 5>;
         using NA = I<(2 * p + 2) % 5>;
         using NB = I<(2 * p + 3) % 5>;
         using FA = I<(2 * p + 4) % 5>;
+        static_assert(qn == 0 || (mode == 0 && qn <= OQ), "quarter loads in normal stages");
         if constexpr (mode == 0) {
             issueB(NB{}, k + 1);
             issueA(FA{}, k + 2);
+            if constexpr (qn == 1) load_c_q_regs(1, oq1);
+            else if constexpr (qn == 2) load_c_q_regs(2, oq2);
+            else if constexpr (qn == 3) load_c_q_regs(3, oq3);
         } else if constexpr (mode == 1) {
             issueB(NB{}, k + 1);
             load_c_q(slot(FA{}), 0);
+        } else if constexpr (OQ > 0) {
+            store_c_q(slot(NB{}), oq1);
+            store_c_q(slot(FA{}), oq2);
         } else {
             load_c_q(slot(NB{}), 1);
             load_c_q(slot(FA{}), 2);
@@ -725,7 +762,8 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
         constexpr int HALF = NMF / 2;
         mfma_range(fa[KL], fb[KL], 0, HALF);
         if constexpr (mode != 2) {
-            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(mode == 0 ? LA : QLD));
+            // the next stage has landed; this stage's later loads stay in flight
+            __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(mode == 0 ? LA + (qn ? QLD : 0) : QLD));
             lt_lds_barrier();
             read_frags(NA{}, NB{}, 0, fa[0], fb[0]);
         }
@@ -740,21 +778,33 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
     lt_lds_barrier();
     read_frags(I<0>{}, I<1>{}, 0, fa[0], fb[0]);
 
-    constexpr int RN = (NKR + 3) % 5;           // (nk - 2) % 5 normal stages after the full trips
+    constexpr int RN = (NKR + 3) % 5;           // (nk - 2) % 5
+    // normal stages unrolled after the loop: the last RN (no out quarters), or
+    // the last 10 + RN with the out-quarter loads at nk - 8, nk - 6, nk - 4
+    // (the launcher picks OQ > 0 only for nk >= 12 + RN)
+    constexpr int TL = OQ > 0 ? 10 + RN : RN;
+    using Z = I<0>;
     int k = 0;
-    for (; k + 5 <= nk - 2; k += 5) {
-        kst(I<0>{}, I<0>{}, k);
-        kst(I<1>{}, I<0>{}, k + 1);
-        kst(I<2>{}, I<0>{}, k + 2);
-        kst(I<3>{}, I<0>{}, k + 3);
-        kst(I<4>{}, I<0>{}, k + 4);
+    for (; k + 5 <= nk - 2 - TL; k += 5) {
+        kst(I<0>{}, Z{}, k, Z{});
+        kst(I<1>{}, Z{}, k + 1, Z{});
+        kst(I<2>{}, Z{}, k + 2, Z{});
+        kst(I<3>{}, Z{}, k + 3, Z{});
+        kst(I<4>{}, Z{}, k + 4, Z{});
     }
-    if constexpr (RN > 0) kst(I<0>{}, I<0>{}, k);
-    if constexpr (RN > 1) kst(I<1>{}, I<0>{}, k + 1);
-    if constexpr (RN > 2) kst(I<2>{}, I<0>{}, k + 2);
-    if constexpr (RN > 3) kst(I<3>{}, I<0>{}, k + 3);
-    kst(I<RN>{}, I<1>{}, k + RN);
-    kst(I<(RN + 1) % 5>{}, I<2>{}, k + RN + 1);
+    // tail stage i (stage k + i) loads out quarter q at i = TL - 8 + 2q
+    auto tail = [&](auto IDX) __attribute__((always_inline)) {
+        constexpr int i = decltype(IDX)::value;
+        constexpr int d = i - (TL - 8);
+        constexpr int q = (OQ > 0 && d >= 2 && d % 2 == 0 && d / 2 <= OQ) ? d / 2 : 0;
+        kst(I<i % 5>{}, Z{}, k + i, I<q>{});
+    };
+    [&]<int... Is>(std::integer_sequence<int, Is...>) __attribute__((always_inline)) {
+        (tail(I<Is>{}), ...);
+    }(std::make_integer_sequence<int, TL>{});
+    k += TL;
+    kst(I<RN>{}, I<1>{}, k, Z{});
+    kst(I<(RN + 1) % 5>{}, I<2>{}, k + 1, Z{});
     constexpr int PL = (RN + 1) % 5;            // phase of the last stage
     using Q0 = I<(2 * PL + 2) % 5>;
     using Q1 = I<(2 * PL + 3) % 5>;
@@ -872,15 +922,21 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
         load_prefix(2, pv2);
         load_prefix(3, pv3);
     }
-    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(2 * QLD + PF));     // quarter 0
+    // quarters loaded from memory after quarter 0: 1 and 2 (OQ == 0), and 3
+    // (OQ < 3, issued below)
+    constexpr int Q12 = OQ > 0 ? 0 : 2 * QLD;
+    constexpr int Q3L = OQ > 2 ? 0 : QLD;
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(Q12 + PF));         // quarter 0
     lt_lds_barrier();
-    load_c_q(slot(Q3{}), 3);
+    if constexpr (OQ > 2) store_c_q(slot(Q3{}), oq3);
+    else load_c_q(slot(Q3{}), 3);
     sums(slot(Q0{}), 0);
-    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? 3 * ITQ + QLD : 2 * QLD));   // quarter 1 (+ prefix 0)
+    // quarter 1 (+ prefix 0)
+    __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? 3 * ITQ + Q3L : (OQ > 0 ? Q3L : 2 * QLD)));
     lt_lds_barrier();
     write_back(slot(Q0{}), 0, pv0);
     sums(slot(Q1{}), 1);
-    if (interior) __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? 2 * ITQ + QLD + SQ : QLD + SQ));
+    if (interior) __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(RES ? 2 * ITQ + Q3L + SQ : Q3L + SQ));
     else __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));         // quarter 2 (+ prefix 1)
     lt_lds_barrier();
     write_back(slot(Q1{}), 1, pv1);
@@ -908,12 +964,16 @@ hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16
     u16 *rsd = res ? res->resid : nullptr;
     const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
     const bool kt = L % BK != 0;
-#define LT_RING(NKR, KT, R)                                                                  \
-    launch(&k_gemm_ring<BJ, WGJ, WGT, GROUP_J, NKR, KT, R>, grid, block, stream, y, ntj, (int)ntt, \
-           T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
+    // out quarters in registers need an unrolled tail of 10 + (nk - 2) % 5
+    // normal stages
+    const bool oq = LT_RING_OQ > 0 && nk >= 12 + (nk - 2) % 5;
+#define LT_RING(NKR, KT, R, Q)                                                               \
+    launch(&k_gemm_ring<BJ, WGJ, WGT, GROUP_J, NKR, KT, R, Q>, grid, block, stream, y, ntj,     \
+           (int)ntt, T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
+#define LT_RING_Q(NKR, KT, R) (oq ? LT_RING(NKR, KT, R, LT_RING_OQ) : LT_RING(NKR, KT, R, 0))
 #define LT_RING_K(NKR)                                                                       \
-    (kt ? (res ? LT_RING(NKR, true, true) : LT_RING(NKR, true, false))                      \
-        : (res ? LT_RING(NKR, false, true) : LT_RING(NKR, false, false)))
+    (kt ? (res ? LT_RING_Q(NKR, true, true) : LT_RING_Q(NKR, true, false))                  \
+        : (res ? LT_RING_Q(NKR, false, true) : LT_RING_Q(NKR, false, false)))
     hipError_t e;
     switch (nk % 5) {
     case 0: e = LT_RING_K(0); break;
@@ -923,6 +983,7 @@ hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16
     default: e = LT_RING_K(4); break;
     }
 #undef LT_RING_K
+#undef LT_RING_Q
 #undef LT_RING
     return e;
 }
@@ -985,8 +1046,9 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
         // alignment and 32-bit tile offsets (T = 8192: 130 vs 136 us)
         auto small = [&](int64_t ld) { return (int64_t)256 * ld * 2 < ((int64_t)1 << 31); };
         if (L > 2 * BK && vec16 && small(ld_out) &&
-            (!res || (small(res->ld_prefix) && small(res->ld_resid))))
+            (!res || (small(res->ld_prefix) && small(res->ld_resid)))) {
             return launch_ring<256, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, stream);
+        }
         return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     }
     if (tiles(128, 128) > 256)
