@@ -1059,6 +1059,11 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
         return launch_cfg<128, 128, 4, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     if (tiles(64, 128) >= 224)
         return launch_cfg<64, 128, 2, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
+    // narrow windows at small T (the 896-column shard at T = 256: 56 tiles of
+    // 64 x 64): 32 x 64 tiles of two waves put twice as many workgroups on
+    // the W stream
+    if (tiles(64, 64) < 128)
+        return launch_cfg<32, 64, 1, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     return launch_cfg<64, 64, 2, 2, 4, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
 }
 

@@ -8,9 +8,7 @@
 //   T <= skinny_max  -> one weight-streaming launch per 64 tokens (32 when
 //                       L > 1024) (k_skinny)
 //   T >  skinny_max  -> k_sum_rmsnorm into a scratch latent, then k_gemm
-//                       (several partials below 1024 tokens: k_sum_partials
-//                       into the scratch first, normalised there in place;
-//                       one partial without the norm: k_gemm reads it as is).
+//                       (one partial without the norm: k_gemm reads it as is).
 // lt_latent_tail_residual runs the same path with the decoder layer's
 // residual update fused into the epilogue of the projection kernel.
 // The pages' own fallback is silent ([PR51253 Implementation, item 2]); a
@@ -35,11 +33,6 @@
 namespace {
 
 constexpr int64_t kDefaultSkinnyMax = 64;
-// Below this token count several partials are summed by their own kernel
-// before the norm (fewer than 64 tiles of 16 tokens for the norm kernel;
-// measured: T = 256 with 8 partials 13.8 vs 18.6 us, T = 128 with 4 partials
-// 14.4 vs 15.6; at T = 1024 and 2048 the extra launch costs what it saves).
-constexpr int64_t kPreSumMaxT = 1024;
 
 std::atomic<int64_t> g_skinny_max{-1};
 // timing events of lt_set_kernel_events, per calling thread
@@ -365,19 +358,8 @@ int tail_impl(const void *partials, int n_partials, int64_t T, int64_t L, const 
     int st = fixed ? noalloc_scratch(&buf) : ensure_scratch((size_t)tl * 2, s, &buf);
     if (st != LT_OK) return st;
     uint16_t *y = static_cast<uint16_t *>(buf);
-    if (n_partials > 1 && T < kPreSumMaxT) {
-        // Few 16-token tiles: the sum+RMSNorm kernel would pull every
-        // partial of a tile through one CU.  The partials are summed first
-        // by an elementwise kernel over the whole latent (same order of
-        // fp32 additions, same bits), then normalised in place.
-        if (lt::launch_sum_partials(part, tl, n_partials, tl, y, s) != hipSuccess)
-            return LT_ERR_HIP;
-        if (nw && lt::launch_sum_rmsnorm(y, tl, 1, T, (int)L, nw, eps, y, s) != hipSuccess)
-            return LT_ERR_HIP;
-    } else if (lt::launch_sum_rmsnorm(part, tl, n_partials, T, (int)L, nw, eps, y, s) !=
-               hipSuccess) {
+    if (lt::launch_sum_rmsnorm(part, tl, n_partials, T, (int)L, nw, eps, y, s) != hipSuccess)
         return LT_ERR_HIP;
-    }
     if (!record_hook(g_ev_before, s)) return LT_ERR_HIP;
     if (lt::launch_gemm(y, T, (int)L, Wn, (int)n, outn, ld_out, res, s) != hipSuccess)
         return LT_ERR_HIP;

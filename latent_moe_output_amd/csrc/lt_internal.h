@@ -30,11 +30,6 @@ hipError_t launch_skinny(const uint16_t *part, int64_t pstride, int P, int T, in
 // Largest token count one skinny launch handles for latent width L.
 int skinny_tokens_per_launch(int L);
 
-// s[i] = bf16(sum_p part[p][i]) for i < count (partial stride pstride, count
-// a multiple of 8, rows 16-byte aligned): the partial sum alone.
-hipError_t launch_sum_partials(const uint16_t *part, int64_t pstride, int P, int64_t count,
-                               uint16_t *s, hipStream_t stream);
-
 // Partial sum + RMSNorm into a packed [T][L] bf16 latent (y may be part
 // itself when P == 1).
 hipError_t launch_sum_rmsnorm(const uint16_t *part, int64_t pstride, int P, int64_t T,

@@ -87,8 +87,10 @@ constexpr int latent_stage_bytes() { return 16 * TT * NI * 512; }
 // rows keep whatever the LDS held.  That is harmless wherever rows >= Tv are
 // never stored: every output of an MFMA depends on one row of each operand,
 // so stale rows reach only outputs of their own row.
+// With SKIP, blocks that hold no row of [rlo, Tv) are not loaded either.
 template <int TT, int NI, int AUX = 0, bool SKIP = false>
-__device__ __forceinline__ void latent_stage(const u16 *__restrict__ tile, int Tv, int L, char *lds)
+__device__ __forceinline__ void latent_stage(const u16 *__restrict__ tile, int Tv, int L, char *lds,
+                                             int rlo = 0)
 {
     static_assert((NI & (NI - 1)) == 0, "slots per row must be a power of two");
     constexpr int SPR = 32 * NI;                  // 16-byte slots per staged row
@@ -97,7 +99,7 @@ __device__ __forceinline__ void latent_stage(const u16 *__restrict__ tile, int T
 #pragma unroll
     for (int k = 0; k < TT * NI; ++k) {
         const int m = KW * k + w;                 // 1 KB block of the staging area
-        if (SKIP && 64 * m / SPR >= Tv) continue;   // wave-uniform
+        if (SKIP && (64 * m / SPR >= Tv || (64 * m + 63) / SPR < rlo)) continue;   // wave-uniform
         const int slot = 64 * m + l;
         const int row = slot / SPR, c = (slot % SPR) ^ (row & 15);
         const uint32_t off = c < (L >> 3) ? (uint32_t)(row * L + c * 8) * 2u : LT_OOB;

@@ -268,13 +268,13 @@ def test_shards_concatenate_bit_exact(T):
 def test_split_partials_bit_exact(T, H, norm, L):
     """[X, Y, -Y] and [X/2, X/2] give the same bits as [X].  With the norm off
     the large-token path multiplies one partial in place and sums several
-    first, so this also ties the two routes together; below 1024 tokens
-    several partials are summed by their own kernel before the norm, from
-    1024 on inside the norm kernel (both sides of that threshold are here);
-    on the weight-streaming path (T <= 64) one partial is staged through LDS
-    (two tiles at a time past 32 tokens) while several are summed in
-    registers.  The one-partial result is checked against the oracle on
-    sampled rows."""
+    first, so this also ties the two routes together; the norm kernel splits
+    a 16-token tile over 1..16 workgroups depending on T (T = 130 to 2048
+    here), staging one partial straight into LDS and summing several in
+    registers; on the weight-streaming path (T <= 64) one partial is staged
+    through LDS (two tiles at a time past 32 tokens) while several are summed
+    in registers.  The one-partial result is checked against the oracle on
+    three rows."""
     from oracle import oracle
 
     wl = synth.Workload("split", T=T, L=L, H=H, P=1, c0=0, n=H, ld_out=H, norm=norm)
