@@ -18,8 +18,8 @@ rotates through enough copies of its partials/out to cycle >= 512 MB.
 
 Printed: ONE JSON line on stdout.  `value` is the whole-job throughput:
 algorithmic flops of the K timed steps / wall-clock time between two device
-synchronisations.  The timed steps run as a HIP graph (G sweeps captured
-once, each call on its own W copy and rotation set, replayed K/G times), the
+synchronisations.  The timed steps run as a HIP graph (one sweep captured
+once, each call on its own W copy and rotation set, replayed K times), the
 way a serving loop launches them; `value_direct_launch` is the same K steps
 launched call by call from Python.  Per-T figures come from a separate
 instrumented pass: HIP events recorded on the benchmark stream around each
@@ -27,14 +27,25 @@ call and, through lt_set_kernel_events, around its projection kernel, each
 call queued behind a short GPU spin so that host launch time stays outside
 the events; `graph_call_us` is each T on its own: its rotation sets captured
 into one graph (each call on its own W copy) and replayed, elapsed time per
-call.  `roofline` is for the dominant kernel (k_gemm_ring at
-T=8192); `roofline_skinny` for the weight-streaming kernel at T <= 16;
-`configs` times the column-shard workloads (T=256 with 8 partials, T=8191
-with 4 partials, with and without the norm, 896-column windows) against
-their rooflines.  `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample of the T=8192 call on this host's cores.  `roofline.traffic` is the GEMM's HBM bytes per
-launch from the committed rocprofv3 counter summary under profiles/, or null
-once the GEMM sources differ from the ones those counters were taken on.
+call (its `w_stream_gbps` is the W window over that time).  `roofline` is
+for the dominant kernel (k_gemm_ring at T=8192); `roofline_skinny` for the
+weight-streaming kernel at T <= 16, whose W-window rate is the top-level
+`w_stream_gbps`; `context.single_launch_floor` times a probe launch of the
+same shape that only streams the W window (and an empty one).  `configs`
+times the column-shard workloads (T=256 with 8 partials, T=8191 with 4
+partials, with and without the norm, 896-column windows) and `attn_res` the
+AttnRes zero-block call (hidden 7168, every switch on) against their
+rooflines.  `cpu_baseline` times the fp64 CPU oracle (median of three runs)
+on a bounded sample of the T=8192 call on this host's cores.
+`roofline.traffic` is the GEMM's HBM bytes per launch from the committed
+rocprofv3 counter summary under profiles/, or null once the GEMM sources
+differ from the ones those counters were taken on.
+
+    python bench.py --workload NAME --steps K
+
+times one workload alone (decodeN, shard, ragged, ragged_nonorm, prefill,
+attn_resN) and prints one JSON line; it is what the profiles under
+profiles/ run.
 """
 from __future__ import annotations
 
@@ -176,8 +187,57 @@ def context_pass(binding, hip, stream, sh, sets, wpool, norm_w, reps=20):
         ctx["warm_same_buffers"] = warm
         hip.destroy(a)
         hip.destroy(b)
+    ctx["single_launch_floor"] = launch_floor(hip, stream, sh, wpool)
     ctx["clocks"] = gpu_clocks()
     return ctx
+
+
+def launch_floor(hip, stream, sh, wpool, reps=10):
+    """What one launch at the weight-streaming kernel's shape (256 workgroups
+    of 512 threads, one 57,344-byte share of the W window each) costs back to
+    back when it does nothing but stream the W window into LDS (probe kernel
+    of libltprobe.so, each launch on its own W copy), and when its body is
+    empty.  The decode call cannot be faster than the stream probe."""
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "latent_moe_output_amd", "probe", "libltprobe.so"))
+    lib.ltp_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                               ctypes.c_void_p]
+    lib.ltp_empty.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    nwg, nthr = 256, 512
+    share = 2 * H * L // nwg                         # 57,344 bytes: 28 W rows
+    res = {}
+    for name, one in (("stream_w_window", lambda i: lib.ltp_stream(wpool[i % len(wpool)].data_ptr(),
+                                                                    share, nwg, nthr, sh)),
+                      ("empty", lambda i: lib.ltp_empty(nwg, nthr, sh))):
+        R = len(wpool)
+        for i in range(R):
+            assert one(i) == 0
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(R):
+                assert one(i) == 0
+        with torch.cuda.stream(stream):
+            g.replay()
+            a, b = hip.event(), hip.event()
+            hip.record(a, sh)
+            for _ in range(reps):
+                g.replay()
+            hip.record(b, sh)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(a, b) * 1e3 / (reps * R)
+        hip.destroy(a)
+        hip.destroy(b)
+        res[name] = {"us_per_launch": round(us, 3)}
+        del g
+    w = 2 * H * L
+    res["stream_w_window"]["gbps"] = round(w / res["stream_w_window"]["us_per_launch"] / 1e3, 1)
+    res["stream_w_window"]["frac_of_hbm_roofline"] = round(
+        w / HBM_PEAK / (res["stream_w_window"]["us_per_launch"] * 1e-6), 4)
+    res["shape"] = "%d workgroups x %d threads, %d bytes each, back to back in a graph of %d " \
+                   "launches (own W copy each)" % (nwg, nthr, share, len(wpool))
+    return res
 
 
 def gpu_clocks():
@@ -438,9 +498,10 @@ def single_workload(name, steps):
     print(json.dumps(dict(workload=name, **res)), flush=True)
 
 
-def cpu_baseline(d, target_s=12.0):
+def cpu_baseline(d, target_s=4.0):
     """The fp64 oracle as it stands on this host's cores, on the first S tokens
-    of the T=8192 call (S sized for ~target_s seconds of work)."""
+    of the T=8192 call (S sized for ~target_s seconds of work), timed three
+    times (the median is reported)."""
     from oracle import oracle
 
     oracle.build(force=False)
@@ -452,9 +513,12 @@ def cpu_baseline(d, target_s=12.0):
     cal = time.perf_counter() - t0
     S = int(max(cal_T, min(8192, cal_T * target_s / max(cal, 1e-6))))
     S = max(cal_T, (S // 16) * 16)
-    t0 = time.perf_counter()
-    oracle.latent_tail(d["partials"][:, :S], d["norm_w"], EPS, d["W"], 0, H, d["out"][:S])
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.latent_tail(d["partials"][:, :S], d["norm_w"], EPS, d["W"], 0, H, d["out"][:S])
+        runs.append(time.perf_counter() - t0)
+    dt = sorted(runs)[1]
     # the same oracle on one thread, on a sample a sixteenth the size
     S1 = max(16, (S // 16) // 16 * 16)
     t0 = time.perf_counter()
@@ -469,8 +533,10 @@ def cpu_baseline(d, target_s=12.0):
         "cores": threads,
         "kind": "oracle",
         "sample": "first %d of the 8192 tokens of the T=8192 call (L=1024, n=7168, one "
-                  "partial, RMSNorm on), fp64 C oracle, %d OpenMP threads, %.2f s" % (S, threads, dt),
+                  "partial, RMSNorm on), fp64 C oracle, %d OpenMP threads, median of 3 runs "
+                  "(%.2f s)" % (S, threads, dt),
         "seconds": dt,
+        "seconds_runs": [round(x, 3) for x in runs],
         "tokens": S,
         "cpu_model": cpu_model(),
         "single_thread": {"value": flops_of(S1) / dt1 / 1e12, "unit": "TFLOP/s",
@@ -495,7 +561,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=4.0)
     ap.add_argument("--workload", default=None,
                     help="time one workload alone and exit (decodeN, shard, ragged, "
                          "ragged_nonorm, prefill, attn_resN); for profilers")
@@ -569,7 +635,12 @@ def main():
     # the Python launch overhead from the measurement, not any GPU work.
     K = args.steps
     nT = len(T_SWEEP)
-    G = max(g for g in range(1, 17) if K % g == 0)
+    # One sweep per graph: a replay's host-side submission (14 nodes) then
+    # overlaps the GPU's work on the previous one.  With 10 sweeps per graph
+    # the first replay's submission (140 nodes) sat unhidden inside the timed
+    # region: at K = 20 the graph read 0.386 ms per step against 0.354 for
+    # the same calls launched directly, and within 1 % of it at K = 200.
+    G = 1
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=stream):
@@ -659,7 +730,7 @@ def main():
             "kernel_us": round(kern_us[T], 3),
             "call_us_median": round(float(np.median(c)), 3),
             "tflops": round(f / call_us[T] / 1e6, 2),
-            "w_stream_gbps": round(2 * H * L / call_us[T] / 1e3, 1),
+            "w_stream_gbps": round(2 * H * L / graph_us[T] / 1e3, 1),
             "alg_gbps": round(b / call_us[T] / 1e3, 1),
             "roofline_us": round(roof_us, 3),
             "bound": "hbm" if b / HBM_PEAK > f / MFMA_BF16_PEAK else "mfma",
@@ -676,7 +747,6 @@ def main():
     context = context_pass(binding, hip, stream, sh, sets, wpool, norm_w)
 
     total_flops = K * sum(flops_of(T) for T in T_SWEEP)
-    total_w = K * nT * 2 * H * L
     value = total_flops / wall / 1e12
 
     Tg = max(T_SWEEP)
@@ -749,7 +819,10 @@ def main():
             "T_sweep": T_SWEEP, "L": L, "H": H, "n": H, "c0": 0, "n_partials": P,
             "skinny_max": binding.lt_get_skinny_max_tokens(),
         },
-        "w_stream_gbps": round(total_w / wall / 1e9, 1),
+        "w_stream_gbps": round(roofline_skinny["achieved"] * (2 * H * L)
+                               / roofline_skinny["bytes_per_launch_avg"], 1),
+        "w_stream_note": "W-window bytes (2*n*L) per decode launch (T <= 16) / its back-to-back "
+                         "time; roofline_skinny has the same launches against all their bytes",
         "launch": "HIP graph of %d sweeps (%d calls), replayed %d times" % (G, G * nT, K // G),
         "value_direct_launch": round(total_flops / wall_direct / 1e12, 2),
         "ms_per_step_direct_launch": round(wall_direct / K * 1e3, 4),

@@ -81,5 +81,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "k_probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libltprobe.so")
+
+
+def build_probe() -> str:
+    """libltprobe.so: the benchmark's launch and stream probes (not part of
+    the tail's ABI)."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *COMMON, "-shared", PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed on %s:\n%s" % (PROBE_SRC, res.stdout + res.stderr))
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe())
