@@ -120,7 +120,7 @@ class Hip:
         self.lib.hipEventDestroy(ev)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_tsweep_L1024_H7168_hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_by_workload.md")
 GEMM_SOURCES = [os.path.join(ROOT, "latent_moe_output_amd", "csrc", f)
                 for f in ("k_gemm.hip", "lt_device.h")]
 
