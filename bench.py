@@ -18,10 +18,12 @@ rotates through enough copies of its partials/out to cycle >= 512 MB.
 
 Printed: ONE JSON line on stdout.  `value` is the whole-job throughput:
 algorithmic flops of the K timed steps / wall-clock time between two device
-synchronisations.  The timed steps run as a HIP graph (one sweep captured
-once, each call on its own W copy and rotation set, replayed K times), the
-way a serving loop launches them; `value_direct_launch` is the same K steps
-launched call by call from Python.  Per-T figures come from a separate
+synchronisations.  The timed steps run as HIP graphs of ten sweeps (each
+call on its own W copy and rotation set, so a replay cycles the whole W pool)
+replayed back to back right after the W warmup sweeps, the way a serving loop
+launches them; `value_direct_launch` is the same K steps launched call by call
+from Python just before, from a GPU that was idle while the graphs were
+captured (and so starts at its idle clocks).  Per-T figures come from a separate
 instrumented pass: HIP events recorded on the benchmark stream around each
 call and, through lt_set_kernel_events, around its projection kernel, each
 call queued behind a short GPU spin so that host launch time stays outside
@@ -623,40 +625,39 @@ def main():
         counter[0] += 1
         return binding.lt_latent_tail(p, P, T, L, norm_w, EPS, W, H, 0, H, o, H, sh)
 
-    # ---- warmup
-    for s in range(args.warmup):
-        for T in T_SWEEP:
-            binding.check(call(T, s))
-    torch.cuda.synchronize()
-
-    # ---- timed region: the sweep captured once into a HIP graph of G steps
-    # (every call reads its own W copy and rotation set), replayed K / G times.
-    # The graph is how a serving loop launches these calls; replay removes
-    # the Python launch overhead from the measurement, not any GPU work.
+    # ---- graphs: the sweep captured into HIP graphs of G = 10 steps (every
+    # call reads its own W copy and rotation set, so one replay cycles the
+    # whole 705 MB W pool and leaves nothing in the 256 MB Infinity Cache for
+    # the next), one of K mod G steps, and one of the W warmup steps.  The
+    # graph is how a serving loop launches these calls; replay removes the
+    # Python launch overhead from the measurement, not any GPU work.
     K = args.steps
     nT = len(T_SWEEP)
-    # One sweep per graph: a replay's host-side submission (14 nodes) then
-    # overlaps the GPU's work on the previous one.  With 10 sweeps per graph
-    # the first replay's submission (140 nodes) sat unhidden inside the timed
-    # region: at K = 20 the graph read 0.386 ms per step against 0.354 for
-    # the same calls launched directly, and within 1 % of it at K = 200.
-    G = 1
-    graph = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph, stream=stream):
-        for s in range(G):
-            for T in T_SWEEP:
-                binding.check(call(T, s))
-    graph.replay()                                   # one untimed replay
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K // G):
-        graph.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
+    G = min(10, K)
 
-    # ---- the same K steps launched call by call from Python, for reference
+    def capture(nsweeps, first):
+        if nsweeps <= 0:
+            return None
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for s_ in range(first, first + nsweeps):
+                for T in T_SWEEP:
+                    binding.check(call(T, s_))
+        return g
+
+    g_warm = capture(args.warmup, 0)
+    graph = capture(G, args.warmup)
+    g_rem = capture(K % G, args.warmup + G)
+    torch.cuda.synchronize()
+
+    # ---- the same K steps launched call by call from Python, for reference.
+    # It runs first, from a GPU that sat idle while the graphs were captured:
+    # after an idle spell the sweep runs about 10 % slower for its first few
+    # milliseconds, however it is launched, and the timed region below must
+    # not start in that state (at K = 20 it lasts 8 ms; with only the W
+    # warmup sweeps before it the graph read 0.393 ms per step, and 0.353
+    # on a GPU kept busy).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
@@ -664,6 +665,21 @@ def main():
             binding.check(call(T, s))
     torch.cuda.synchronize()
     wall_direct = time.perf_counter() - t0
+
+    # ---- warmup: the W warmup sweeps, replayed right before the timed region
+    if g_warm is not None:
+        g_warm.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
+    t0 = time.perf_counter()
+    for _ in range(K // G):
+        graph.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
 
     # ---- instrumented pass (not part of `value`): HIP events around every
     # call and, through lt_set_kernel_events, around its projection kernel
@@ -823,7 +839,10 @@ def main():
                                / roofline_skinny["bytes_per_launch_avg"], 1),
         "w_stream_note": "W-window bytes (2*n*L) per decode launch (T <= 16) / its back-to-back "
                          "time; roofline_skinny has the same launches against all their bytes",
-        "launch": "HIP graph of %d sweeps (%d calls), replayed %d times" % (G, G * nT, K // G),
+        "launch": "HIP graph of %d sweeps (%d calls) replayed %d times%s, right after the %d "
+                  "warmup sweeps (also a graph), which follow the direct-launch pass" % (
+                      G, G * nT, K // G, " + one of %d sweeps" % (K % G) if K % G else "",
+                      args.warmup),
         "value_direct_launch": round(total_flops / wall_direct / 1e12, 2),
         "ms_per_step_direct_launch": round(wall_direct / K * 1e3, 4),
         "per_T": per_T,
