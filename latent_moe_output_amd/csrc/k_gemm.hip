@@ -519,67 +519,82 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
     }
 }
 
-// Square tiles (BJ = BT) with the operand stream on a ring of five LDS slots.
-// A K stage is two half-stages of BJ x 64 bf16 (32 KB at BJ = 256): A (W
-// rows) and B (tokens).  Half-stage h (stage h / 2) lives in slot h % 5, so
-// while stage k is multiplied out of two slots the other three hold stage
-// k + 1 and A of stage k + 2: 96 KB of operands in flight per workgroup
-// against the 64 KB of two whole 64 KB stages, in the same 160 KB of LDS.
-// Each stage fetches B of stage k + 1 and A of stage k + 2 into the slots
-// stage k - 1 left.  The `out` tile moves through four slots in quarters of
-// BT / 4 token rows: quarter 0 is fetched during stage nk - 2 (in place of A
-// of stage nk), quarters 1 and 2 during the last stage and quarter 3 once it
-// is done.  NKR = nk % 5 fixes, at compile time, the slot every stage and
-// quarter uses.  The `out` tile is read and written once, so those loads and
-// stores are marked non-temporal (same box, alternating runs: T = 8192 about
-// 4-8 % faster).  Same tile order, swizzles, K order and epilogue arithmetic
-// as k_gemm, so the results are bit-identical to it.
-template <int BJ, int WGJ, int WGT, int GROUP_J, int NKR, bool KTAIL, bool RES, int OQ>
-__global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int ntj, int ntt,
-                                                              int64_t T, int L, int n,
-                                                              const u16 *__restrict__ Wn,
-                                                              u16 *__restrict__ outn, int64_t ld_out,
-                                                              const u16 *prefn, int64_t ld_pre,
-                                                              u16 *resn, int64_t ld_res)
+// Tiles of BJ W rows x 256 tokens with the operand stream on a ring of five
+// LDS slots.  A K stage is two half-stages of 64 bf16 per row: A (BJ W rows,
+// 32 KB at BJ = 256) and B (256 tokens, 32 KB).  Half-stage h (stage h / 2)
+// lives in slot h % 5, so while stage k is multiplied out of two slots the
+// other three hold stage k + 1 and A of stage k + 2: 96 KB of operands in
+// flight per workgroup against the 64 KB of two whole 64 KB stages, in the
+// same 160 KB of LDS.  Each stage fetches B of stage k + 1 and A of stage
+// k + 2 into the slots stage k - 1 left.  The `out` tile moves through four
+// slots in quarters of 64 token rows: quarter 0 is fetched during stage
+// nk - 2 (in place of A of stage nk), quarters 1 and 2 during the last stage
+// and quarter 3 once it is done.  NKR = nk % 5 fixes, at compile time, the
+// slot every stage and quarter uses.  The `out` tile is read and written
+// once, so those loads and stores are marked non-temporal (same box,
+// alternating runs: T = 8192 about 4-8 % faster).  Same tile order,
+// swizzles, K order and epilogue arithmetic as k_gemm, so the results are
+// bit-identical to it.
+//
+// The five slots live at namespace scope so that the full-width (BJ = 256)
+// and half-width (BJ = 128) tile bodies of one kernel share them.
+constexpr int RING_BT = 256;                  // tokens per ring tile
+constexpr int RING_SLOT = RING_BT * ROWB;     // bytes of one slot (a 256-row half-stage)
+constexpr int RING_CUS = 256;                 // compute units of the chip
+__shared__ __attribute__((aligned(1024))) char ring_sl0[RING_SLOT];
+__shared__ __attribute__((aligned(1024))) char ring_sl1[RING_SLOT];
+__shared__ __attribute__((aligned(1024))) char ring_sl2[RING_SLOT];
+__shared__ __attribute__((aligned(1024))) char ring_sl3[RING_SLOT];
+__shared__ __attribute__((aligned(1024))) char ring_sl4[RING_SLOT];
+
+// Full 256 x 256 tiles of a ring launch over G of them.  When the last round
+// would leave at least half of the compute units idle (0 < G mod 256 <= 128,
+// G > 256), its tiles are handed out as two 128 x 256 halves each, so that
+// every CU takes part in that round and each does half the work: the
+// workgroups of the halves come last in the grid and start as the CUs finish
+// their last full tile.  The halves keep the K order of every output, so the
+// results are the same bit for bit.
+__host__ __device__ constexpr int ring_full_tiles(int G)
 {
-    constexpr int BT = BJ;
+    return (G > RING_CUS && G % RING_CUS != 0 && G % RING_CUS <= RING_CUS / 2)
+               ? G - G % RING_CUS
+               : G;
+}
+
+// Position of workgroup b in an order of G work items that gives each of the
+// 8 XCDs (workgroup b runs on XCD b mod 8) one contiguous range.
+__device__ __forceinline__ int xcd_contiguous(int b, int G)
+{
+    const int xcd = b % NUM_XCD, idx = b / NUM_XCD;
+    const int q8 = G / NUM_XCD, r8 = G % NUM_XCD;
+    return (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+}
+
+// One BJ x 256 tile (W rows j0.., tokens t0..) of the slot-ring GEMM.
+template <int BJ, int WGJ, int WGT, int NKR, bool KTAIL, bool RES, int OQ>
+__device__ __forceinline__ void ring_tile(const u16 *__restrict__ Y, int64_t T, int L, int n,
+                                          const u16 *__restrict__ Wn, u16 *__restrict__ outn,
+                                          int64_t ld_out, const u16 *prefn, int64_t ld_pre,
+                                          u16 *resn, int64_t ld_res, int j0, int64_t t0)
+{
+    constexpr int BT = RING_BT;
     constexpr int NW = WGJ * WGT;
     constexpr int NT = 64 * NW;
     constexpr int MJ = BJ / WGJ / 32, MT = BT / WGT / 32;
     constexpr int LR = 8 * NW;
-    constexpr int LA = BJ / LR;                 // direct loads per thread per operand half-stage
-    constexpr int SLOT = BJ * ROWB;             // one operand's share of a K stage
+    constexpr int LA = BJ / LR;                 // direct loads per thread per W half-stage
+    constexpr int LB = BT / LR;                 // and per token half-stage
+    constexpr int SLOT = RING_SLOT;
     constexpr int NFR = MJ + MT, NMF = MJ * MT;
-    static_assert(MJ >= 1 && MT == 4 && LA * LR == BJ, "tile shape");
-    __shared__ __attribute__((aligned(1024))) char sl0[SLOT];
-    __shared__ __attribute__((aligned(1024))) char sl1[SLOT];
-    __shared__ __attribute__((aligned(1024))) char sl2[SLOT];
-    __shared__ __attribute__((aligned(1024))) char sl3[SLOT];
-    __shared__ __attribute__((aligned(1024))) char sl4[SLOT];
+    static_assert(MJ >= 1 && MT == 4 && LA * LR == BJ && LB * LR == BT && BJ <= BT, "tile shape");
     auto slot = [&](auto S) __attribute__((always_inline)) -> char * {
         constexpr int s = decltype(S)::value;
-        if constexpr (s == 0) return sl0;
-        else if constexpr (s == 1) return sl1;
-        else if constexpr (s == 2) return sl2;
-        else if constexpr (s == 3) return sl3;
-        else return sl4;
+        if constexpr (s == 0) return ring_sl0;
+        else if constexpr (s == 1) return ring_sl1;
+        else if constexpr (s == 2) return ring_sl2;
+        else if constexpr (s == 3) return ring_sl3;
+        else return ring_sl4;
     };
-
-    // ---- tile coordinates, buffer resources and fragment rows as in k_gemm
-    const int G = ntj * ntt;
-    const int b = blockIdx.x;
-    const int xcd = b % NUM_XCD, idx = b / NUM_XCD;
-    const int q8 = G / NUM_XCD, r8 = G % NUM_XCD;
-    const int nb = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
-    const int gsize = GROUP_J * ntt;
-    const int gid = nb / gsize;
-    const int first_j = gid * GROUP_J;
-    const int gj = min(ntj - first_j, GROUP_J);
-    const int within = nb - gid * gsize;
-    const int tj = first_j + within % gj;
-    const int tt = within / gj;
-    const int j0 = tj * BJ;
-    const int64_t t0 = (int64_t)tt * BT;
 
     const int tid = threadIdx.x;
     const int l = tid & 63;
@@ -594,32 +609,33 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
     const __amdgpu_buffer_rsrc_t ra = lt_rsrc(Wn + (int64_t)j0 * L, (uint32_t)rows_a * row_bytes);
     const __amdgpu_buffer_rsrc_t rb = lt_rsrc(Y + t0 * L, (uint32_t)rows_b * row_bytes);
 
-    // direct loads as in k_gemm (both operands have BJ rows, so they share
-    // the offsets); the K offset goes in the scalar offset, which keeps the
-    // unrolled stages from holding one address register per stage
+    // direct loads as in k_gemm (both operands have row stride L, so the W
+    // half-stage uses the first LA of the token half-stage's offsets); the K
+    // offset goes in the scalar offset, which keeps the unrolled stages from
+    // holding one address register per stage
     const int lrow = 8 * w + (l >> 3);
     const int lslot = l & 7;
-    uint32_t off[LA];
-    int ch[LA];
+    uint32_t off[LB];
+    int ch[LB];
 #pragma unroll
-    for (int q = 0; q < LA; ++q) {
+    for (int q = 0; q < LB; ++q) {
         const int row = LR * q + lrow;
         ch[q] = lslot ^ swz8(row);
         off[q] = (uint32_t)row * row_bytes + (uint32_t)ch[q] * 16u;
     }
-    auto issue = [&](const __amdgpu_buffer_rsrc_t &rs, auto S, int s) __attribute__((always_inline)) {
+    auto issue = [&](const __amdgpu_buffer_rsrc_t &rs, auto S, auto NQ, int s) __attribute__((always_inline)) {
         char *dst = slot(S);
         const uint32_t kbyte = (uint32_t)s * ROWB;
 #pragma unroll
-        for (int q = 0; q < LA; ++q) {
+        for (int q = 0; q < decltype(NQ)::value; ++q) {
             uint32_t vo = off[q];
             if (KTAIL && s * CPR + ch[q] >= nchunk) vo = OOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + (LR * q + 8 * w) * ROWB),
                                                      16, vo, (int)kbyte, 0, 0);
         }
     };
-    auto issueA = [&](auto S, int s) __attribute__((always_inline)) { issue(ra, S, s); };
-    auto issueB = [&](auto S, int s) __attribute__((always_inline)) { issue(rb, S, s); };
+    auto issueA = [&](auto S, int s) __attribute__((always_inline)) { issue(ra, S, I<LA>{}, s); };
+    auto issueB = [&](auto S, int s) __attribute__((always_inline)) { issue(rb, S, I<LB>{}, s); };
 
     const int hsel = l >> 5;
     const int arow = wj * (BJ / WGJ) + perm32(l & 31);
@@ -664,7 +680,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
         }
     };
 
-    // out tile in quarters of BT/4 token rows, one slot each
+    // out tile in quarters of BT/4 token rows (BJ columns), one slot each
     constexpr int CPRE = BJ / 8;
     constexpr int RPQ = BT / 4;
     constexpr int QCH = RPQ * CPRE;
@@ -951,15 +967,58 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
     write_back(slot(Q3{}), 3, pv3);
 }
 
-template <int BJ, int WGJ, int WGT, int GROUP_J>
+// The ring GEMM over ntj x ntt tiles of 256 x 256: XCD-contiguous ranges of
+// the grouped tile order as in k_gemm; with a split last round (see
+// ring_full_tiles) the halves follow the full tiles, both halves of a tile on
+// the same XCD.
+template <int WGJ, int WGT, int GROUP_J, int NKR, bool KTAIL, bool RES, int OQ>
+__global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int ntj, int ntt,
+                                                              int64_t T, int L, int n,
+                                                              const u16 *__restrict__ Wn,
+                                                              u16 *__restrict__ outn, int64_t ld_out,
+                                                              const u16 *prefn, int64_t ld_pre,
+                                                              u16 *resn, int64_t ld_res)
+{
+    constexpr int BJ = RING_BT;
+    const int G = ntj * ntt;
+    const int nfull = ring_full_tiles(G);
+    const int b = blockIdx.x;
+    int nb, hj = 0;                             // tile in the grouped order, W-row offset
+    if (b < nfull) {
+        nb = xcd_contiguous(b, nfull);
+    } else {
+        const int h = xcd_contiguous(b - nfull, 2 * (G - nfull));
+        nb = nfull + h / 2;
+        hj = (h & 1) ? BJ / 2 : 0;
+    }
+    const int gsize = GROUP_J * ntt;
+    const int gid = nb / gsize;
+    const int first_j = gid * GROUP_J;
+    const int gj = min(ntj - first_j, GROUP_J);
+    const int within = nb - gid * gsize;
+    const int tj = first_j + within % gj;
+    const int tt = within / gj;
+    const int j0 = tj * BJ + hj;
+    const int64_t t0 = (int64_t)tt * RING_BT;
+    if (b < nfull)
+        ring_tile<BJ, WGJ, WGT, NKR, KTAIL, RES, OQ>(Y, T, L, n, Wn, outn, ld_out, prefn, ld_pre,
+                                                     resn, ld_res, j0, t0);
+    else if (j0 < n)   // the second half of a tile that the window ends in may be empty
+        ring_tile<BJ / 2, WGJ, WGT, NKR, KTAIL, RES, OQ>(Y, T, L, n, Wn, outn, ld_out, prefn,
+                                                         ld_pre, resn, ld_res, j0, t0);
+}
+
+template <int WGJ, int WGT, int GROUP_J>
 hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 *outn,
                        int64_t ld_out, const Resid *res, hipStream_t stream)
 {
-    const int ntj = (n + BJ - 1) / BJ;
-    const int64_t ntt = (T + BJ - 1) / BJ;
+    const int ntj = (n + RING_BT - 1) / RING_BT;
+    const int64_t ntt = (T + RING_BT - 1) / RING_BT;
     const int nk = (L + BK - 1) / BK;
-    if (nk < 3) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(ntj * ntt)), block(64 * WGJ * WGT);
+    if (nk < 3 || (int64_t)ntj * ntt > (1 << 30)) return hipErrorInvalidValue;
+    const int G = (int)(ntj * ntt);
+    const int nfull = ring_full_tiles(G);
+    const dim3 grid((unsigned)(nfull + 2 * (G - nfull))), block(64 * WGJ * WGT);
     const u16 *pre = res ? res->prefix : nullptr;
     u16 *rsd = res ? res->resid : nullptr;
     const int64_t ldp = res ? res->ld_prefix : 0, ldr = res ? res->ld_resid : 0;
@@ -968,7 +1027,7 @@ hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16
     // normal stages
     const bool oq = LT_RING_OQ > 0 && nk >= 12 + (nk - 2) % 5;
 #define LT_RING(NKR, KT, R, Q)                                                               \
-    launch(&k_gemm_ring<BJ, WGJ, WGT, GROUP_J, NKR, KT, R, Q>, grid, block, stream, y, ntj,     \
+    launch(&k_gemm_ring<WGJ, WGT, GROUP_J, NKR, KT, R, Q>, grid, block, stream, y, ntj,         \
            (int)ntt, T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
 #define LT_RING_Q(NKR, KT, R) (oq ? LT_RING(NKR, KT, R, LT_RING_OQ) : LT_RING(NKR, KT, R, 0))
 #define LT_RING_K(NKR)                                                                       \
@@ -1047,7 +1106,7 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
         auto small = [&](int64_t ld) { return (int64_t)256 * ld * 2 < ((int64_t)1 << 31); };
         if (L > 2 * BK && vec16 && small(ld_out) &&
             (!res || (small(res->ld_prefix) && small(res->ld_resid)))) {
-            return launch_ring<256, 4, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, stream);
+            return launch_ring<4, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, stream);
         }
         return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     }

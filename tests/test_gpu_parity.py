@@ -130,6 +130,13 @@ def test_large_workload_full(name):
     (2048, 7168, 0, 7176, 1, 1024),    # 16, interior tiles only
     (2000, 7100, 0, 7104, 1, 192),     # 3
     (2000, 7100, 0, 7104, 1, 128),     # 2: two-stage kernel
+    # ring launches whose last round is split into 128 x 256 halves (280 tiles:
+    # 256 whole, 24 as 48 halves): interior, a ragged last column tile whose
+    # second half has 60 columns, and one whose second half is empty (ragged
+    # T, K tail)
+    (2560, 7168, 0, 7176, 1, 1024),
+    (2560, 7100, 0, 7104, 1, 1024),
+    (2500, 7012, 8, 7024, 2, 1096),
 ])
 def test_gemm_tile_shapes(T, n, c0, ld, P, L):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
@@ -254,6 +261,25 @@ def test_shards_concatenate_bit_exact(T):
     part = DevInputs(d)
     for k in range(8):
         binding.check(part.call(wl, c0=k * 224, n=224))
+    _sync()
+    np.testing.assert_array_equal(host(part.out), host(full.out))
+
+
+def test_split_last_round_bit_exact():
+    """A ring launch whose last round runs as half-width tiles (T = 2560 over
+    7168 columns: 280 tiles of 256 x 256, the last 24 as 48 halves) equals,
+    bit for bit, eight 896-column shards that run the 128 x 128 kernel: the
+    halves keep every output's K order."""
+    wl = synth.Workload("split_round", T=2560, L=1024, H=7168, P=1, c0=0, n=7168,
+                        ld_out=7168, part_std=0.7)
+    d = synth.generate(wl, seed=17)
+    full = DevInputs(d)
+    say("split last round: full window")
+    binding.check(full.call(wl))
+    part = DevInputs(d)
+    for k in range(8):
+        say("split last round: shard %d" % k)
+        binding.check(part.call(wl, c0=k * 896, n=896))
     _sync()
     np.testing.assert_array_equal(host(part.out), host(full.out))
 

@@ -77,6 +77,7 @@ CASES = [
     (64, 1024, 1536, 2, 64, 1024, 1544, 1552, 1560, 0),    # forced GEMM at a skinny size
     (100, 1024, 1536, 2, 64, 1024, 1544, 1552, 1560, 1000),  # forced skinny, two launches
     (2000, 1032, 7110, 1, 8, 7100, 7112, 7120, 7128, -1),  # 256 x 256 slot ring, K tail, ragged
+    (2560, 1024, 7100, 1, 8, 7090, 7112, 7120, 7128, -1),  # ring, last round in halves, ragged
 ]
 
 
