@@ -967,11 +967,16 @@ __device__ __forceinline__ void ring_tile(const u16 *__restrict__ Y, int64_t T, 
     write_back(slot(Q3{}), 3, pv3);
 }
 
-// The ring GEMM over ntj x ntt tiles of 256 x 256: XCD-contiguous ranges of
-// the grouped tile order as in k_gemm; with a split last round (see
-// ring_full_tiles) the halves follow the full tiles, both halves of a tile on
-// the same XCD.
-template <int WGJ, int WGT, int GROUP_J, int NKR, bool KTAIL, bool RES, int OQ>
+// The ring GEMM over ntj x ntt tiles of 256 x 256.  Tile order: groups of
+// GROUP_T token panels by every column panel, token panel fastest, so that
+// the tiles an XCD runs at one time share few latent panels and the next
+// tiles on the XCD reuse them (the latent loads cost about twice the W loads
+// per stage otherwise, as the previous order put eight latent panels in
+// each XCD's concurrent tiles; T = 8192 125.7 vs 128.6 us, 4 token panels
+// 126.6, 2 128.6); each XCD takes a contiguous range of that order.  With a
+// split last round (see ring_full_tiles) the halves follow the full tiles,
+// both halves of a tile on the same XCD.
+template <int WGJ, int WGT, int GROUP_T, int NKR, bool KTAIL, bool RES, int OQ>
 __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int ntj, int ntt,
                                                               int64_t T, int L, int n,
                                                               const u16 *__restrict__ Wn,
@@ -991,13 +996,13 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
         nb = nfull + h / 2;
         hj = (h & 1) ? BJ / 2 : 0;
     }
-    const int gsize = GROUP_J * ntt;
+    const int gsize = GROUP_T * ntj;
     const int gid = nb / gsize;
-    const int first_j = gid * GROUP_J;
-    const int gj = min(ntj - first_j, GROUP_J);
+    const int first_t = gid * GROUP_T;
+    const int gt = min(ntt - first_t, GROUP_T);
     const int within = nb - gid * gsize;
-    const int tj = first_j + within % gj;
-    const int tt = within / gj;
+    const int tt = first_t + within % gt;
+    const int tj = within / gt;
     const int j0 = tj * BJ + hj;
     const int64_t t0 = (int64_t)tt * RING_BT;
     if (b < nfull)
@@ -1008,7 +1013,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restr
                                                          ld_pre, resn, ld_res, j0, t0);
 }
 
-template <int WGJ, int WGT, int GROUP_J>
+template <int WGJ, int WGT, int GROUP_T>
 hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16 *outn,
                        int64_t ld_out, const Resid *res, hipStream_t stream)
 {
@@ -1027,7 +1032,7 @@ hipError_t launch_ring(const u16 *y, int64_t T, int L, const u16 *Wn, int n, u16
     // normal stages
     const bool oq = LT_RING_OQ > 0 && nk >= 12 + (nk - 2) % 5;
 #define LT_RING(NKR, KT, R, Q)                                                               \
-    launch(&k_gemm_ring<WGJ, WGT, GROUP_J, NKR, KT, R, Q>, grid, block, stream, y, ntj,         \
+    launch(&k_gemm_ring<WGJ, WGT, GROUP_T, NKR, KT, R, Q>, grid, block, stream, y, ntj,         \
            (int)ntt, T, L, n, Wn, outn, ld_out, pre, ldp, rsd, ldr)
 #define LT_RING_Q(NKR, KT, R) (oq ? LT_RING(NKR, KT, R, LT_RING_OQ) : LT_RING(NKR, KT, R, 0))
 #define LT_RING_K(NKR)                                                                       \
@@ -1106,7 +1111,7 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
         auto small = [&](int64_t ld) { return (int64_t)256 * ld * 2 < ((int64_t)1 << 31); };
         if (L > 2 * BK && vec16 && small(ld_out) &&
             (!res || (small(res->ld_prefix) && small(res->ld_resid)))) {
-            return launch_ring<4, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, stream);
+            return launch_ring<4, 2, 8>(y, T, L, Wn, n, outn, ld_out, res, stream);
         }
         return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     }
