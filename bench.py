@@ -376,7 +376,7 @@ def time_workload(binding, hip, stream, sh, wl, wpool, reps=10):
         "T": wl.T, "n_partials": wl.P, "c0": wl.c0, "n": wl.n, "ld_out": wl.ld_out,
         "norm": wl.norm,
         "path": ("skinny" if binding.lt_path_for(wl.T, wl.n) == 1 else
-                 ("sum+norm, gemm" if wl.norm or wl.P > 1 else "gemm")),
+                 ("sum+norm, gemm" if wl.norm else "sum, gemm" if wl.P > 1 else "gemm")),
         "call_us": round(us, 3),
         "tflops": round(f / us / 1e6, 2),
         "alg_gbps": round(byt / us / 1e3, 1),

@@ -974,8 +974,9 @@ __device__ __forceinline__ void ring_tile(const u16 *__restrict__ Y, int64_t T, 
 // per stage otherwise, as the previous order put eight latent panels in
 // each XCD's concurrent tiles; T = 8192 125.7 vs 128.6 us, 4 token panels
 // 126.6, 2 128.6); each XCD takes a contiguous range of that order.  With a
-// split last round (see ring_full_tiles) the halves follow the full tiles,
-// both halves of a tile on the same XCD.
+// split last round (see ring_full_tiles) the halves follow the full tiles in
+// the same kind of order, so the two halves of a tile share an XCD wherever
+// the XCD ranges of halves have even length (as at T = 8192).
 template <int WGJ, int WGT, int GROUP_T, int NKR, bool KTAIL, bool RES, int OQ>
 __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm_ring(const u16 *__restrict__ Y, int ntj, int ntt,
                                                               int64_t T, int L, int n,
