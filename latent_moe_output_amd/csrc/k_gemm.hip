@@ -46,7 +46,8 @@
 //  * The largest tiles (256 x 256) run k_gemm_ring, the same GEMM with the
 //    operand stream on a ring of five 32 KB slots (half a K stage each), so
 //    that 96 KB of operands are in flight instead of 64 KB; its `out` tile
-//    moves in quarters through the slots.
+//    moves in quarters through the slots, and a last round that would leave
+//    half of the CUs idle runs as 128 x 256 half tiles.
 // Each output element's accumulation order depends on L only (K ascending in
 // 16-wide MFMA slices), not on c0, n or the tile shape.
 #include <type_traits>
@@ -88,6 +89,15 @@ __device__ __forceinline__ int swz8(int r)
     return ((r >> 1) & 1) | (((r ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
 }
 
+// Position of workgroup b in an order of G work items that gives each of the
+// 8 XCDs (workgroup b runs on XCD b mod 8) one contiguous range.
+__device__ __forceinline__ int xcd_contiguous(int b, int G)
+{
+    const int xcd = b % NUM_XCD, idx = b / NUM_XCD;
+    const int q8 = G / NUM_XCD, r8 = G % NUM_XCD;
+    return (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+}
+
 // Argument order: everything the tile set-up needs comes first, within the
 // 14 argument dwords that are preloaded into scalar registers at wave launch
 // (the library is built with kernel-argument preloading); the residual
@@ -125,10 +135,7 @@ __global__ __launch_bounds__(64 * WGJ * WGT) void k_gemm(const u16 *__restrict__
 
     // ---- tile coordinates: XCD-contiguous ranges, then GROUP_J-wide groups
     const int G = ntj * ntt;
-    const int b = blockIdx.x;
-    const int xcd = b % NUM_XCD, idx = b / NUM_XCD;
-    const int q8 = G / NUM_XCD, r8 = G % NUM_XCD;
-    const int nb = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+    const int nb = xcd_contiguous(blockIdx.x, G);
     const int gsize = GROUP_J * ntt;
     const int gid = nb / gsize;
     const int first_j = gid * GROUP_J;
@@ -559,15 +566,6 @@ __host__ __device__ constexpr int ring_full_tiles(int G)
     return (G > RING_CUS && G % RING_CUS != 0 && G % RING_CUS <= RING_CUS / 2)
                ? G - G % RING_CUS
                : G;
-}
-
-// Position of workgroup b in an order of G work items that gives each of the
-// 8 XCDs (workgroup b runs on XCD b mod 8) one contiguous range.
-__device__ __forceinline__ int xcd_contiguous(int b, int G)
-{
-    const int xcd = b % NUM_XCD, idx = b / NUM_XCD;
-    const int q8 = G / NUM_XCD, r8 = G % NUM_XCD;
-    return (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
 }
 
 // One BJ x 256 tile (W rows j0.., tokens t0..) of the slot-ring GEMM.

@@ -168,11 +168,13 @@ def test_constant_rows_normalise_to_weight(H):
             assert np.all(synth.bf16_bits_to_f64(out[t]) == 0.0)
 
 
-@pytest.mark.parametrize("T,H", [(5, 8), (9, 520), (33, 4104), (4, 8192), (2048, 7168),
-                                 (8192, 1024)])
+@pytest.mark.parametrize("T,H", [(5, 8), (9, 520), (11, 1544), (3, 2048), (6, 3000), (2, 4096),
+                                 (33, 4104), (4, 8192), (2048, 7168), (8192, 1024)])
 def test_ragged_and_large_shapes(T, H):
     """Rows that end inside a lane's chunk range (H not a multiple of 512),
-    the widest row, and prefill-sized token counts; all switches on."""
+    the widest row, and prefill-sized token counts; all switches on.  The
+    widths cover every workgroup shape of the kernel: 1, 2, 4 and 8 waves
+    per row with one 16-byte chunk per lane, and 8 waves with two."""
     from oracle import oracle
 
     prefix, delta, block, w, out0 = _inputs(T, H, seed=T + H)
