@@ -46,7 +46,7 @@ extern "C" {
 /* Status codes. */
 #define LT_OK 0
 #define LT_ERR_INVALID_ARG 1   /* an argument is out of range, NULL or overlaps */
-#define LT_ERR_UNSUPPORTED 2   /* legal in principle, outside what this build handles */
+#define LT_ERR_UNSUPPORTED 2   /* legal in principle, outside what this library handles */
 #define LT_ERR_NO_MEMORY 3     /* scratch could not be (re)allocated */
 #define LT_ERR_HIP 4           /* a HIP call or kernel launch failed */
 #define LT_ERR_SCRATCH_LIMIT 5 /* lt_latent_tail_noalloc: T*L beyond its fixed scratch */
