@@ -117,6 +117,33 @@ def test_contract_matrix(H, T, has_delta, write_block, norm):
     _compare(got, ref, norm, "T=%d H=%d d=%s b=%s n=%s" % (T, H, has_delta, write_block, norm))
 
 
+def _random_cases(count=48, seed=77):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(count):
+        T = int(np.exp(rng.uniform(0, np.log(3000))))
+        H = 8 * int(rng.integers(1, 1025))
+        sw = rng.random(3) < 0.6
+        cases.append((i, T, H, bool(sw[0]), bool(sw[1]), bool(sw[2])))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: "r%02d_T%d_H%d_%d%d%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[5]))
+def test_random_shapes(case):
+    """48 seeded random (tokens, hidden, switches) draws over the whole
+    supported range (H a multiple of 8 up to 8192), against the oracle."""
+    from oracle import oracle
+
+    i, T, H, has_delta, write_block, norm = case
+    prefix, delta, block, w, out0 = _inputs(T, H, seed=900 + i)
+    idx = (i * 5) % SLOTS if write_block else -1
+    args = (prefix, delta if has_delta else None, block if write_block else None, idx,
+            w if norm else None, EPS32)
+    say("attn_res random %d: T=%d H=%d delta=%s block=%d norm=%s" % (i, T, H, has_delta, idx, norm))
+    _compare(_run(*args, out0), oracle.attn_res_zero_block(*args), norm, "random %d" % i)
+
+
 def test_hand_worked_example_bit_exact():
     """The hand-derived values of tests/golden/attn_res_hand_example.txt (two
     exact ties of the storage round trip, a -0 output) through the GPU.  The
