@@ -508,6 +508,41 @@ def test_graph_capture_and_replay(T):
     del g
 
 
+def test_split_ring_graph_replay():
+    """The ring launch whose last round runs as half tiles (T = 2560 over
+    7168 columns), captured into a HIP graph after lt_reserve and replayed
+    three times with eager work in between: every replay equals the eager
+    call bit for bit."""
+    import torch
+
+    wl = synth.Workload("split_graph", T=2560, L=1024, H=7168, P=1, c0=0, n=7168,
+                        ld_out=7168, part_std=0.7)
+    di = DevInputs(synth.generate(wl, seed=23))
+    say("split ring graph: eager")
+    binding.check(di.call(wl))
+    _sync()
+    want = host(di.out)
+    s = torch.cuda.Stream()
+    assert binding.lt_reserve(wl.T, wl.L, s) == binding.LT_OK
+    di.reset_out()
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    say("split ring graph: capture")
+    with torch.cuda.graph(g, stream=s):
+        status = di.call(wl, stream=torch.cuda.current_stream())
+    assert status == binding.LT_OK
+    for rep in range(3):
+        di.reset_out()
+        _sync()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        say("split ring graph: replay %d" % rep)
+        g.replay()
+        _sync()
+        np.testing.assert_array_equal(host(di.out), want)
+        del junk
+    del g
+
+
 def test_graphs_of_several_shapes_survive_scratch_growth():
     """Graph replay at varying shapes ([PR50593 Implementation, item 4]):
     graphs captured at T = 8 (weight streaming), 100 and 777 (sum+RMSNorm
