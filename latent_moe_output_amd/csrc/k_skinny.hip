@@ -44,7 +44,10 @@
 //    dimension; the idle columns of a partly filled token tile cost nothing
 //    that matters here, the matrix cores are far from busy.
 //  * The KW per-wave partial products are added in LDS in wave order and
-//    written with one bf16 rounding onto the window.  The residual form (RES)
+//    written with one bf16 rounding onto the window, with device-scope
+//    stores (lt_store8_dev; back to back T = 1 5.09 -> 4.83 us, T = 16
+//    5.43 -> 5.11, T = 64 9.54 -> 8.96: the store is the call's last round
+//    trip, and a device-coherent one completes sooner).  The residual form (RES)
 //    also writes bf16(prefix + out') with the prefix prefetched alongside
 //    `out` ([PR50593 Key source snippets, `forward_attn_residual`]).
 //
@@ -53,6 +56,7 @@
 #include "lt_internal.h"
 #include "lt_latent.h"
 #include "lt_launch.h"
+#include "lt_store.h"
 
 namespace lt {
 namespace {
@@ -213,13 +217,13 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
         u32x2_t nv;
         nv[0] = lt_pack2(lt_bf_lo(opre[0]) + d[0], lt_bf_hi(opre[0]) + d[1]);
         nv[1] = lt_pack2(lt_bf_lo(opre[1]) + d[2], lt_bf_hi(opre[1]) + d[3]);
-        *reinterpret_cast<u32x2_t *>(o) = nv;
+        lt_store8_dev(o, nv);
         if constexpr (RES) {
             u32x2_t rv;
 #pragma unroll
             for (int e = 0; e < 2; ++e)
                 rv[e] = lt_pack2(lt_bf_lo(ppre[e]) + lt_bf_lo(nv[e]), lt_bf_hi(ppre[e]) + lt_bf_hi(nv[e]));
-            *reinterpret_cast<u32x2_t *>(resn + (int64_t)te * ld_res + j0 + jl) = rv;
+            lt_store8_dev(resn + (int64_t)te * ld_res + j0 + jl, rv);
         }
     } else {
 #pragma unroll
@@ -227,12 +231,12 @@ __global__ __launch_bounds__(64 * KW) void k_skinny(const u16 *__restrict__ part
             if (jl + a < rows) {
                 const float v = lt_bf_lo((uint32_t)o[a]) + d[a];
                 const u16 onew = (u16)(lt_pack2(v, 0.f) & 0xFFFFu);
-                o[a] = onew;
+                lt_store2_dev(o + a, onew);
                 if constexpr (RES) {
                     const int64_t jj = j0 + jl + a;
                     const float r = lt_bf_lo((uint32_t)prefn[(int64_t)te * ld_pre + jj]) +
                                     lt_bf_lo((uint32_t)onew);
-                    resn[(int64_t)te * ld_res + jj] = (u16)(lt_pack2(r, 0.f) & 0xFFFFu);
+                    lt_store2_dev(resn + (int64_t)te * ld_res + jj, (u16)(lt_pack2(r, 0.f) & 0xFFFFu));
                 }
             }
         }
