@@ -1104,14 +1104,18 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
     // Below a round of 64 x 128 tiles, 64 x 64 tiles put twice as many
     // workgroups on the W stream (T = 128: 6.3 vs 7.7 us).
     auto tiles = [&](int bj, int bt) { return (int64_t)((n + bj - 1) / bj) * ((T + bt - 1) / bt); };
-    if (tiles(256, 256) >= 224) {
-        // the slot ring needs at least three K stages and the LDS epilogue's
-        // alignment and 32-bit tile offsets (T = 8192: 130 vs 136 us)
-        auto small = [&](int64_t ld) { return (int64_t)256 * ld * 2 < ((int64_t)1 << 31); };
-        if (L > 2 * BK && vec16 && small(ld_out) &&
-            (!res || (small(res->ld_prefix) && small(res->ld_resid)))) {
-            return launch_ring<4, 2, 8>(y, T, L, Wn, n, outn, ld_out, res, stream);
-        }
+    // the slot ring needs at least three K stages and the LDS epilogue's
+    // alignment and 32-bit tile offsets (T = 8192: 130 vs 136 us)
+    auto small = [&](int64_t ld) { return (int64_t)256 * ld * 2 < ((int64_t)1 << 31); };
+    const bool ring_ok = L > 2 * BK && vec16 && small(ld_out) &&
+                         (!res || (small(res->ld_prefix) && small(res->ld_resid)));
+    // 256 x 256 tiles from about one round of them, and on the ring also
+    // where two-stage 128 x 128 tiles would need a second round of two per
+    // CU: one ring round of 140-196 tiles beats two such rounds (n = 7168,
+    // T = 1280 / 1536 / 1792: 32.4 / 33.7 / 35.2 vs 39.6 / 41.2 / 43.7 us per
+    // call; T = 1152, 504 tiles in one round: 31.6 vs 29.3, so not there)
+    if (tiles(256, 256) >= 224 || (ring_ok && tiles(128, 128) > 512)) {
+        if (ring_ok) return launch_ring<4, 2, 8>(y, T, L, Wn, n, outn, ld_out, res, stream);
         return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     }
     if (tiles(128, 128) > 256)

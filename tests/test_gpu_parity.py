@@ -137,6 +137,10 @@ def test_large_workload_full(name):
     (2560, 7168, 0, 7176, 1, 1024),
     (2560, 7100, 0, 7104, 1, 1024),
     (2500, 7012, 8, 7024, 2, 1096),
+    # one ring round below 224 tiles, where 128 x 128 tiles would need two
+    # rounds of two per CU: 140 tiles (interior), 168 (ragged T and n, K tail)
+    (1280, 7168, 0, 7176, 1, 1024),
+    (1300, 7100, 16, 7120, 2, 1096),
 ])
 def test_gemm_tile_shapes(T, n, c0, ld, P, L):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
