@@ -191,7 +191,87 @@ def context_pass(binding, hip, stream, sh, sets, wpool, norm_w, reps=20):
         hip.destroy(b)
     ctx["single_launch_floor"] = launch_floor(hip, stream, sh, wpool)
     ctx["clocks"] = gpu_clocks()
+    ctx["power_under_load"] = power_under_load(binding, stream, sh, sets, wpool, norm_w)
     return ctx
+
+
+def under_profiler():
+    return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
+
+
+def power_under_load(binding, stream, sh, sets, wpool, norm_w, seconds=2.5, samples=3):
+    """Socket power and per-XCD shader clocks (`amd-smi metric -p -c`) while
+    the T = 8192 call (norm + GEMM, own W copy per call) runs back to back
+    for a few seconds, next to the package power cap (`rocm-smi
+    --showmaxpower`): whether the GEMM runs at the nominal clock the MFMA
+    peak assumes or at a power-limited one.  None under a profiler or where
+    the tools are missing."""
+    import re
+    import subprocess
+    import threading
+    import time
+    import torch
+
+    if under_profiler():
+        return None
+
+    def sample():
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                               timeout=30)
+        except (OSError, subprocess.SubprocessError):
+            return None
+        watts = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+        gfx = re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", r.stdout)
+        if not watts or not gfx:
+            return None
+        return {"socket_power_w": float(watts[0]),
+                "gfx_clk_mhz": [float(x) for x in gfx]}
+
+    T = 8192
+    p, _ = sets[T][0]
+    o = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    R = 8
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(R):
+            binding.check(binding.lt_latent_tail(p, P, T, L, norm_w, EPS, wpool[i % len(wpool)], H,
+                                                 0, H, o, H, sh))
+    reps = int(seconds / (R * 125e-6))
+
+    def work():
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                g.replay()
+
+    th = threading.Thread(target=work)
+    th.start()
+    time.sleep(0.8)
+    got = []
+    for _ in range(samples):
+        x = sample()
+        if x is not None:
+            got.append(x)
+        time.sleep(0.2)
+    th.join()
+    torch.cuda.synchronize()
+    del g, o
+    cap = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower"], capture_output=True, text=True, timeout=20)
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", r.stdout)
+        cap = float(m.group(1)) if m else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if not got:
+        return None
+    clk = [sum(x["gfx_clk_mhz"]) / len(x["gfx_clk_mhz"]) for x in got]
+    return {"socket_power_w": [x["socket_power_w"] for x in got],
+            "gfx_clk_mhz_mean_over_xcds": [round(c, 1) for c in clk],
+            "power_cap_w": cap,
+            "workload": "T=8192 call (norm + GEMM, n=7168) back to back for about %.1f s, "
+                        "sampled %d times after 0.8 s" % (seconds, len(got))}
 
 
 def launch_floor(hip, stream, sh, wpool, reps=10):
@@ -249,7 +329,7 @@ def gpu_clocks():
     the GPU in the child before rocm-smi's launcher hands over to python."""
     import subprocess
 
-    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+    if under_profiler():
         return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
