@@ -41,6 +41,15 @@ hipError_t launch_sum_rmsnorm(const uint16_t *part, int64_t pstride, int P, int6
 hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
                        uint16_t *outn, int64_t ld_out, const Resid *res, hipStream_t stream);
 
+// The GEMM on 256 x 128 tiles with a ping-pong wave schedule (no residual
+// form; `out` 16-byte aligned with ld_out % 8 == 0).  Used where the tile
+// count is within [PP_MIN_TILES, PP_MAX_TILES] (about one round of such
+// tiles) and at least four K stages; gemm_pp_fits() says whether a call is.
+constexpr int PP_MIN_TILES = 140, PP_MAX_TILES = 240;
+bool gemm_pp_fits(int64_t T, int L, int n, int64_t ld_out);
+hipError_t launch_gemm_pp(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
+                          uint16_t *outn, int64_t ld_out, hipStream_t stream);
+
 // AttnRes zero-block path: per token row t < T of width H (H % 8 == 0,
 // H <= 8192, rows 16-byte aligned), p' = bf16(prefix + delta) (delta may be
 // NULL), written back to prefix when delta is set and to block_slot +

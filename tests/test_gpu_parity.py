@@ -116,9 +116,9 @@ def test_large_workload_full(name):
     (130, 7168, 24, 7200, 2, 1032),    # 64 x 128 with a K tail
     (129, 7100, 3, 7112, 1, 1096),     # 64 x 64 with a K tail, ragged T and n
     (2000, 7100, 64, 7168, 1, 1032),   # 256 x 256, LDS epilogue, K tail (L % 128 != 0)
-    (1000, 7100, 32, 7136, 2, 1096),   # 128 x 128 / 2 stages with a K tail
+    (1000, 7100, 33, 7136, 2, 1096),   # 128 x 128 / 2 stages with a K tail (unaligned window)
     (500, 7100, 0, 7104, 1, 1160),     # 128 x 128 / 4 stages with a K tail
-    (1500, 4000, 0, 4008, 1, 2048),    # widest latent, 128 x 128 / 2 stages (384 tiles)
+    (1500, 4000, 1, 4008, 1, 2048),    # widest latent, 128 x 128 / 2 stages (384 tiles)
     (900, 7100, 6, 7112, 2, 1024),     # 128 x 128 / 2 stages, 2 tiles per CU (392 tiles)
     (320, 7100, 5, 7112, 1, 1032),     # 128 x 128 / 4 stages where 64 x 128 needs 2 rounds
     # 256 x 256 on the five-slot ring: every phase of the last K stage
@@ -141,6 +141,20 @@ def test_large_workload_full(name):
     # rounds of two per CU: 140 tiles (interior), 168 (ragged T and n, K tail)
     (1280, 7168, 0, 7176, 1, 1024),
     (1300, 7100, 16, 7120, 2, 1096),
+    # 256 x 128 ping-pong tiles (about one round of 140 .. 240 of them, aligned
+    # window): every nk mod 3 with and without a K tail, ragged T (down to 10
+    # rows in the last token tile, so its second out quarter is empty) and
+    # ragged n (a chunk that crosses the window's end), the widest latent
+    # and the fewest K stages it takes (4)
+    (1024, 7168, 0, 7176, 1, 1024),    # 224 tiles, interior, nk = 16
+    (1000, 7100, 32, 7136, 2, 1096),   # nk = 18, K tail, ragged T and n
+    (700, 6000, 8, 6016, 1, 1000),     # nk = 16, K tail, 144 tiles
+    (900, 5000, 24, 5032, 3, 1088),    # nk = 17
+    (650, 7100, 16, 7120, 1, 1032),    # nk = 17, K tail, 10 rows in the last token tile
+    (1500, 4000, 0, 4008, 1, 2048),    # nk = 32
+    (600, 7100, 0, 7104, 1, 264),      # nk = 5, K tail
+    (640, 7168, 0, 7176, 1, 256),      # nk = 4
+    (800, 7100, 0, 7104, 1, 1152),     # nk = 18
 ])
 def test_gemm_tile_shapes(T, n, c0, ld, P, L):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
@@ -267,6 +281,29 @@ def test_shards_concatenate_bit_exact(T):
         binding.check(part.call(wl, c0=k * 224, n=224))
     _sync()
     np.testing.assert_array_equal(host(part.out), host(full.out))
+
+
+def test_pingpong_tiles_bit_exact():
+    """The ping-pong 256 x 128 kernel (the full 7168-column window at T = 1000)
+    equals, bit for bit, eight 896-column shards that run the 32 x 64 and
+    128 x 128 kernels, and two unaligned half windows that run 128 x 128."""
+    wl = synth.Workload("pingpong", T=1000, L=1024, H=7176, P=1, c0=0, n=7168,
+                        ld_out=7176, part_std=0.7)
+    d = synth.generate(wl, seed=23)
+    full = DevInputs(d)
+    say("ping-pong tiles: full window")
+    binding.check(full.call(wl))
+    part = DevInputs(d)
+    for k in range(8):
+        say("ping-pong tiles: shard %d" % k)
+        binding.check(part.call(wl, c0=k * 896, n=896))
+    _sync()
+    np.testing.assert_array_equal(host(part.out), host(full.out))
+    odd = DevInputs(d)
+    binding.check(odd.call(wl, c0=0, n=3581))
+    binding.check(odd.call(wl, c0=3581, n=3587))
+    _sync()
+    np.testing.assert_array_equal(host(odd.out), host(full.out))
 
 
 def test_split_last_round_bit_exact():
