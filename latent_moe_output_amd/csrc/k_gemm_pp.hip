@@ -1,5 +1,6 @@
-// k_gemm_pp.hip -- the large-token GEMM on 256 x 128 tiles with a ping-pong
-// wave schedule, for calls that fill about one round of such tiles.
+// k_gemm_pp.hip -- the large-token GEMM on 256 x 128 (or 128 x 128) tiles
+// with a ping-pong wave schedule, for calls that fill about one round of
+// such tiles.
 //
 // Same operation, operand layout, swizzles, K order and epilogue arithmetic
 // as k_gemm.hip (out[t][c0+j] = bf16(out[t][c0+j] + sum_k y[t][k] *
@@ -7,15 +8,16 @@
 // `_shard_up_proj_tail`]), so its results are the same bits.
 //
 // Layout on gfx950:
-//  * Tile: 256 W rows (output columns) x 128 tokens, 8 waves.  Waves 0-3
-//    (group 0) and 4-7 (group 1) each hold one wave per SIMD; wave w owns W
-//    rows 64 (w % 4).. and the 32-token blocks 64 mt + 32 (w / 4), as 2 x 2
-//    tiles of v_mfma_f32_32x32x16_bf16 (W as A, the latent as B).
-//  * K advances 64 at a time through three LDS stage arrays of 48 KB
-//    (filled by direct-to-LDS loads of whole 128-byte lines, XOR-swizzled).
+//  * Tile: BJ = 256 (or 128) W rows (output columns) x 128 tokens, 8 waves.
+//    Waves 0-3 (group 0) and 4-7 (group 1) each hold one wave per SIMD;
+//    wave w owns W rows (BJ / 4) (w % 4).. and the 32-token blocks
+//    64 mt + 32 (w / 4), as BJ / 128 x 2 tiles of v_mfma_f32_32x32x16_bf16
+//    (W as A, the latent as B).
+//  * K advances 64 at a time through three LDS stage arrays of 48 KB (32 KB)
+//    filled by direct-to-LDS loads of whole 128-byte lines, XOR-swizzled.
 //  * Ping-pong: the two groups run the same sequence one phase apart.  In a
 //    memory phase a wave reads all fragments of its stage into registers;
-//    in an MFMA phase it issues the stage's 16 MFMAs back to back.  While
+//    in an MFMA phase it issues the stage's 16 (8) MFMAs back to back.  While
 //    one group of a SIMD's two waves multiplies, the other reads, so the
 //    matrix core of every SIMD has a wave issuing to it in both phases.
 //    Each phase ends with a workgroup barrier (both groups pass the same
@@ -44,23 +46,39 @@
 namespace lt {
 namespace {
 
-constexpr int PP_BJ = 256, PP_BT = 128;
-constexpr int PP_STAGE_A = PP_BJ * ROWB, PP_STAGE = (PP_BJ + PP_BT) * ROWB;   // 48 KB
-constexpr int PP_MJ = 2, PP_MT = 2, PP_BSTR = 64;
+constexpr int PP_BT = 128;                         // tokens per tile
+constexpr int PP_MT = 2, PP_BSTR = 64;             // token blocks per wave, their stride
 constexpr int PP_GROUP_T = 8;                      // token panels per tile group
-constexpr int PP_RPQ = 64, PP_CPRE = PP_BJ / 8;    // out quarter: 64 rows x 32 chunks
-constexpr int PP_QB = PP_RPQ * PP_BJ * 2;          // 32 KB
-constexpr int PP_HL = (PP_BJ + PP_BT) / 64;        // 1 KB loads per wave, half a stage (6)
-constexpr int PP_QL = PP_QB / 4096;                // 1 KB loads per wave, a quarter (8)
-constexpr int PP_NMF = KSL * PP_MJ * PP_MT;        // MFMAs per wave and stage (16)
+constexpr int PP_RPQ = 64;                         // out quarter: 64 token rows
 
-// NKR = nk % 3 fixes which stage array every step uses; KTAIL: L % 64 != 0.
-template <int NKR, bool KTAIL>
+// Tile geometry for BJ W rows (256 or 128) x 128 tokens.
+template <int BJ> struct PPGeo {
+    static constexpr int STAGE_A = BJ * ROWB, STAGE = (BJ + PP_BT) * ROWB;   // 48 / 32 KB
+    static constexpr int NB = (BJ + PP_BT) / 8;    // 1 KB row blocks per stage
+    static constexpr int WR = BJ / 4;              // W rows per wave
+    static constexpr int MJ = WR / 32;             // 32-row W blocks per wave
+    static constexpr int CPRE = BJ / 8;            // 16-byte chunks per out row
+    static constexpr int QB = PP_RPQ * BJ * 2;     // out quarter bytes (32 / 16 KB)
+    static constexpr int HL = NB / 8;              // 1 KB loads per wave, half a stage
+    static constexpr int QL = QB / 4096;           // 1 KB loads per wave, a quarter
+    static constexpr int NMF = KSL * MJ * PP_MT;   // MFMAs per wave and stage
+    static constexpr int NWB = PP_RPQ * CPRE / 512;   // 16-byte stores per thread, a quarter
+    static_assert(HL <= NMF && QL <= NMF, "one load per MFMA at most");
+    static_assert(QB <= STAGE, "an out quarter fits a stage array");
+};
+
+// BJ: W rows per tile (256 or 128); NKR = nk % 3 fixes which stage array
+// every step uses; KTAIL: L % 64 != 0.
+template <int BJ, int NKR, bool KTAIL>
 __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int ntj, int ntt,
                                                  int64_t T, int L, int n,
                                                  const u16 *__restrict__ Wn,
                                                  u16 *__restrict__ outn, int64_t ld_out)
 {
+    using Geo = PPGeo<BJ>;
+    constexpr int PP_BJ = BJ, PP_STAGE_A = Geo::STAGE_A, PP_STAGE = Geo::STAGE;
+    constexpr int PP_MJ = Geo::MJ, PP_CPRE = Geo::CPRE, PP_HL = Geo::HL, PP_QL = Geo::QL;
+    constexpr int PP_NMF = Geo::NMF, PP_WR = Geo::WR, PP_NB = Geo::NB;
     __shared__ __attribute__((aligned(1024))) char st0[PP_STAGE];
     __shared__ __attribute__((aligned(1024))) char st1[PP_STAGE];
     __shared__ __attribute__((aligned(1024))) char st2[PP_STAGE];
@@ -95,8 +113,8 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
     const __amdgpu_buffer_rsrc_t ra = lt_rsrc(Wn + (int64_t)j0 * L, (uint32_t)rows_a * row_bytes);
     const __amdgpu_buffer_rsrc_t rb = lt_rsrc(Y + t0 * L, (uint32_t)rows_b * row_bytes);
 
-    // One 1 KB direct load: block blk (8 stage rows; blocks 0..31 are W rows,
-    // 32..47 tokens) of K stage s into dst.  Lane i writes slot i % 8 of row
+    // One 1 KB direct load: block blk (8 stage rows; the first BJ / 8 blocks
+    // are W rows, the rest tokens) of K stage s into dst.  Lane i writes slot i % 8 of row
     // i / 8 with global chunk (slot ^ swz8(row)); rows past the tile's end
     // and chunks past L read zero.
     auto load1 = [&](char *dst, int blk, int s) __attribute__((always_inline)) {
@@ -113,7 +131,7 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
     // ---- fragments: lane l reads row perm32(l % 32) of each 32-row block,
     // chunk 2 ks + l / 32 of the stage row for K slice ks (offset XOR 32 ks)
     const int hsel = l >> 5;
-    const int arow = 64 * wv + perm32(l & 31);
+    const int arow = PP_WR * wv + perm32(l & 31);
     const int brow = 32 * grp + perm32(l & 31);
     const int xa0 = arow * ROWB + ((hsel ^ swz8(arow)) << 4);
     const int xb0 = PP_STAGE_A + brow * ROWB + ((hsel ^ swz8(brow)) << 4);
@@ -137,8 +155,8 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
 #pragma unroll
         for (int mt = 0; mt < PP_MT; ++mt) acc[mj][mt] = f32x16_t{};
 
-    // ---- out quarter q (token rows 64 q.., 256 columns): 16-byte chunk c of
-    // row r at slot c ^ (r & 31); loaded by the four waves of group 1
+    // ---- out quarter q (token rows 64 q.., BJ columns): 16-byte chunk c of
+    // row r at slot c ^ (r % CPRE); loaded by the four waves of group 1
     const __amdgpu_buffer_rsrc_t rc = lt_rsrc(
         outn + t0 * ld_out, (uint32_t)(((int64_t)max(rows_b - 1, 0) * ld_out + n) * 2));
     auto load_q1 = [&](char *dst, int q, int it) __attribute__((always_inline)) {
@@ -149,9 +167,9 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
             (uint32_t)(((int64_t)(PP_RPQ * q + r) * ld_out + j0 + 8 * c) * 2), 0, 0, LT_NT);
     };
 
-    // MFMA phase: the stage's 16 MFMAs, each followed by one of this phase's
-    // loads (LD: 0 none, 1 this group's half of stage sl into SD, 2 out
-    // quarter q into SD)
+    // MFMA phase: the stage's MFMAs, the first NL of them each followed by
+    // one of this phase's loads (LD: 0 none, 1 this group's half of stage
+    // sl into SD, 2 out quarter q into SD)
     auto mfma_phase = [&](auto LD, auto SD, int sl, int q) __attribute__((always_inline)) {
         constexpr int ld = decltype(LD)::value;
         constexpr int NL = ld == 1 ? PP_HL : (ld == 2 ? PP_QL : 0);
@@ -165,7 +183,7 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
                                                                           acc[mj][mt], 0, 0, 0);
                     const int i = (ks * PP_MJ + mj) * PP_MT + mt;
                     if constexpr (ld == 1) {
-                        if (i < NL) load1(stage(SD), 24 * grp + 4 * i + wv, sl);
+                        if (i < NL) load1(stage(SD), (PP_NB / 2) * grp + 4 * i + wv, sl);
                     } else if constexpr (ld == 2) {
                         if (i < NL) load_q1(stage(SD), q, i);
                     }
@@ -215,9 +233,9 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
     using W0 = I<0>;
     // prologue: stages 0 and 1 by every wave (blocks 8 i + w)
 #pragma unroll
-    for (int i = 0; i < 6; ++i) load1(stage(I<0>{}), 8 * i + w, 0);
+    for (int i = 0; i < PP_HL; ++i) load1(stage(I<0>{}), 8 * i + w, 0);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) load1(stage(I<1>{}), 8 * i + w, 1);
+    for (int i = 0; i < PP_HL; ++i) load1(stage(I<1>{}), 8 * i + w, 1);
     __builtin_amdgcn_s_waitcnt(lt_vm_lgkm0(0));
     barrier();
     if (grp == 0) {
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
     } else {
         // group 1's half of stage 2 (its "MFMA phase of stage -1")
 #pragma unroll
-        for (int i = 0; i < PP_HL; ++i) load1(stage(I<2>{}), 24 + 4 * i + wv, 2);
+        for (int i = 0; i < PP_HL; ++i) load1(stage(I<2>{}), PP_NB / 2 + 4 * i + wv, 2);
         barrier();                            // group 1 runs one phase behind
         for (int s = 0; s < nl; s += 3) {
             step(I<0>{}, WH{}, H{}, I<0>{}, W63{}, s + 3, 0);
@@ -266,9 +284,9 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
         for (int mj = 0; mj < PP_MJ; ++mj)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int c = (64 * wv + 32 * mj + 16 * h + 8 * hsel) >> 3;
+                const int c = (PP_WR * wv + 32 * mj + 16 * h + 8 * hsel) >> 3;
                 u32x4_t *p = reinterpret_cast<u32x4_t *>(qb + brow_q * (PP_BJ * 2) +
-                                                         ((c ^ (brow_q & 31)) << 4));
+                                                         ((c ^ (brow_q & (PP_CPRE - 1))) << 4));
                 u32x4_t ov = *p;
                 const int jc = j0 + 8 * c;
                 if (edge && jc < n && jc + 8 > n && t < T) {
@@ -291,13 +309,14 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
     };
     auto write_back = [&](const char *qb, int q) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 8 * w + 2 * i + (l >> 5), c = l & 31;
+        for (int i = 0; i < Geo::NWB; ++i) {
+            const int idx = 512 * i + (int)threadIdx.x;
+            const int r = idx / PP_CPRE, c = idx % PP_CPRE;
             const int64_t t = t0 + PP_RPQ * q + r;
             const int j = j0 + 8 * c;
             if (t < T && j < n) {
-                const u32x4_t v =
-                    *reinterpret_cast<const u32x4_t *>(qb + r * (PP_BJ * 2) + ((c ^ (r & 31)) << 4));
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(qb + r * (PP_BJ * 2) +
+                                                                     ((c ^ (r & (PP_CPRE - 1))) << 4));
                 if (j + 8 <= n) {
                     __builtin_amdgcn_raw_buffer_store_b128(
                         v, rc, (uint32_t)(((int64_t)(PP_RPQ * q + r) * ld_out + j) * 2), 0, LT_NT);
@@ -322,30 +341,42 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
 
 }  // namespace
 
-bool gemm_pp_fits(int64_t T, int L, int n, int64_t ld_out)
+int gemm_pp_rows(int64_t T, int L, int n, int64_t ld_out)
 {
-    const int64_t tiles = (int64_t)((n + PP_BJ - 1) / PP_BJ) * ((T + PP_BT - 1) / PP_BT);
-    return (L + BK - 1) / BK >= 4 && tiles >= PP_MIN_TILES && tiles <= PP_MAX_TILES &&
-           (int64_t)PP_BT * ld_out * 2 < ((int64_t)1 << 31);
+    if ((L + BK - 1) / BK < 4 || (int64_t)PP_BT * ld_out * 2 >= ((int64_t)1 << 31)) return 0;
+    const int64_t tt = (T + PP_BT - 1) / PP_BT;
+    const int64_t t256 = (int64_t)((n + 255) / 256) * tt, t128 = (int64_t)((n + 127) / 128) * tt;
+    // 128-row tiles (the kernel takes BJ = 128 as well) measured slower than
+    // the four- and two-stage 128 x 128 kernels where they would fill a round
+    // (n = 7168, T = 260 .. 512: 3-8 % per call), so only 256-row tiles run
+    (void)t128;
+    return t256 >= PP_MIN_TILES && t256 <= PP_MAX_TILES ? 256 : 0;
 }
 
-hipError_t launch_gemm_pp(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
-                          uint16_t *outn, int64_t ld_out, hipStream_t stream)
+template <int BJ>
+hipError_t launch_pp_bj(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
+                        uint16_t *outn, int64_t ld_out, hipStream_t stream)
 {
-    const int ntj = (n + PP_BJ - 1) / PP_BJ;
+    const int ntj = (n + BJ - 1) / BJ;
     const int ntt = (int)((T + PP_BT - 1) / PP_BT);
     const int nk = (L + BK - 1) / BK;
-    if (!gemm_pp_fits(T, L, n, ld_out)) return hipErrorInvalidValue;
     const bool kt = L % BK != 0;
     const dim3 grid((unsigned)(ntj * ntt)), block(512);
 #define LT_PP(NKR, KT)                                                                       \
-    launch(&k_gemm_pp<NKR, KT>, grid, block, stream, y, ntj, ntt, T, L, n, Wn, outn, ld_out)
+    launch(&k_gemm_pp<BJ, NKR, KT>, grid, block, stream, y, ntj, ntt, T, L, n, Wn, outn, ld_out)
     switch (nk % 3) {
     case 0: return kt ? LT_PP(0, true) : LT_PP(0, false);
     case 1: return kt ? LT_PP(1, true) : LT_PP(1, false);
     default: return kt ? LT_PP(2, true) : LT_PP(2, false);
     }
 #undef LT_PP
+}
+
+hipError_t launch_gemm_pp(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
+                          uint16_t *outn, int64_t ld_out, hipStream_t stream)
+{
+    if (gemm_pp_rows(T, L, n, ld_out) != 256) return hipErrorInvalidValue;
+    return launch_pp_bj<256>(y, T, L, Wn, n, outn, ld_out, stream);
 }
 
 }  // namespace lt

@@ -117,7 +117,7 @@ def test_large_workload_full(name):
     (129, 7100, 3, 7112, 1, 1096),     # 64 x 64 with a K tail, ragged T and n
     (2000, 7100, 64, 7168, 1, 1032),   # 256 x 256, LDS epilogue, K tail (L % 128 != 0)
     (1000, 7100, 33, 7136, 2, 1096),   # 128 x 128 / 2 stages with a K tail (unaligned window)
-    (500, 7100, 0, 7104, 1, 1160),     # 128 x 128 / 4 stages with a K tail
+    (500, 7100, 3, 7112, 1, 1160),     # 128 x 128 / 4 stages with a K tail
     (1500, 4000, 1, 4008, 1, 2048),    # widest latent, 128 x 128 / 2 stages (384 tiles)
     (900, 7100, 6, 7112, 2, 1024),     # 128 x 128 / 2 stages, 2 tiles per CU (392 tiles)
     (320, 7100, 5, 7112, 1, 1032),     # 128 x 128 / 4 stages where 64 x 128 needs 2 rounds
@@ -155,6 +155,16 @@ def test_large_workload_full(name):
     (600, 7100, 0, 7104, 1, 264),      # nk = 5, K tail
     (640, 7168, 0, 7176, 1, 256),      # nk = 4
     (800, 7100, 0, 7104, 1, 1152),     # nk = 18
+    # aligned windows with fewer than 140 tiles of 256 x 128 (128 x 128 tiles,
+    # four or two stages): every nk mod 3 with and without a K tail, ragged T
+    # (4 rows in the last token tile) and n
+    (300, 7100, 8, 7112, 1, 1000),     # nk = 16, K tail
+    (500, 7100, 0, 7104, 1, 1160),     # nk = 19, K tail
+    (400, 7168, 0, 7176, 2, 1088),     # nk = 17
+    (260, 6000, 16, 6024, 1, 1032),    # nk = 17, K tail, 4 rows in the last token tile
+    (450, 7100, 24, 7128, 1, 1152),    # nk = 18
+    (350, 7000, 0, 7008, 1, 1096),     # nk = 18, K tail
+    (320, 7168, 0, 7176, 1, 1024),     # nk = 16, interior
 ])
 def test_gemm_tile_shapes(T, n, c0, ld, P, L):
     """Each GEMM tile shape the dispatcher picks, on ragged T and n with an
