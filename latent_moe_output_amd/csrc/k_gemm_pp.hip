@@ -1,6 +1,5 @@
-// k_gemm_pp.hip -- the large-token GEMM on 256 x 128 (or 128 x 128) tiles
-// with a ping-pong wave schedule, for calls that fill about one round of
-// such tiles.
+// k_gemm_pp.hip -- the large-token GEMM on 256 x 128 tiles with a ping-pong
+// wave schedule, for calls that fill about one round of such tiles.
 //
 // Same operation, operand layout, swizzles, K order and epilogue arithmetic
 // as k_gemm.hip (out[t][c0+j] = bf16(out[t][c0+j] + sum_k y[t][k] *
@@ -344,13 +343,11 @@ __global__ __launch_bounds__(512) void k_gemm_pp(const u16 *__restrict__ Y, int 
 int gemm_pp_rows(int64_t T, int L, int n, int64_t ld_out)
 {
     if ((L + BK - 1) / BK < 4 || (int64_t)PP_BT * ld_out * 2 >= ((int64_t)1 << 31)) return 0;
-    const int64_t tt = (T + PP_BT - 1) / PP_BT;
-    const int64_t t256 = (int64_t)((n + 255) / 256) * tt, t128 = (int64_t)((n + 127) / 128) * tt;
-    // 128-row tiles (the kernel takes BJ = 128 as well) measured slower than
-    // the four- and two-stage 128 x 128 kernels where they would fill a round
-    // (n = 7168, T = 260 .. 512: 3-8 % per call), so only 256-row tiles run
-    (void)t128;
-    return t256 >= PP_MIN_TILES && t256 <= PP_MAX_TILES ? 256 : 0;
+    // 256-row tiles only: on 128-row tiles (which the kernel also takes) it
+    // measured slower than the four- and two-stage 128 x 128 kernels wherever
+    // it would fill a round (n = 7168, T = 260 .. 512: 3-8 % per call)
+    const int64_t tiles = (int64_t)((n + 255) / 256) * ((T + PP_BT - 1) / PP_BT);
+    return tiles >= PP_MIN_TILES && tiles <= PP_MAX_TILES ? 256 : 0;
 }
 
 template <int BJ>
