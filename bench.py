@@ -858,6 +858,16 @@ def main():
         "avg_launch_us": round(kern_us[Tg], 3),
         "flops_per_launch": flops_of(Tg),
     }
+    # The peak assumes the 2.4 GHz nominal shader clock; under a sustained
+    # load of this call the package sits at its power cap with lower XCD
+    # clocks (context.power_under_load).  The same achieved rate against the
+    # peak scaled to the mean of those clock readings:
+    pul = context.get("power_under_load") or {}
+    clk = pul.get("gfx_clk_mhz_mean_over_xcds")
+    if clk:
+        mhz = sum(clk) / len(clk)
+        roofline["frac_at_loaded_clock"] = round(g_ach / (MFMA_BF16_PEAK * mhz / 2400.0), 4)
+        roofline["loaded_clock_mhz"] = round(mhz, 1)
     # decode kernel: back-to-back launches (each on its own W copy) between two
     # events, so the events' own cost does not land on a 6 us kernel.  A spin
     # kernel queued first keeps the GPU busy while the host enqueues all of
