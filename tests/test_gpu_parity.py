@@ -559,17 +559,18 @@ def test_graph_capture_and_replay(T):
     del g
 
 
-def test_split_ring_graph_replay():
+@pytest.mark.parametrize("T", [2560, 1000])
+def test_split_ring_graph_replay(T):
     """The ring launch whose last round runs as half tiles (T = 2560 over
-    7168 columns), captured into a HIP graph after lt_reserve and replayed
-    three times with eager work in between: every replay equals the eager
-    call bit for bit."""
+    7168 columns) and the ping-pong 256 x 128 kernel (T = 1000), each
+    captured into a HIP graph after lt_reserve and replayed three times with
+    eager work in between: every replay equals the eager call bit for bit."""
     import torch
 
-    wl = synth.Workload("split_graph", T=2560, L=1024, H=7168, P=1, c0=0, n=7168,
+    wl = synth.Workload("split_graph", T=T, L=1024, H=7168, P=1, c0=0, n=7168,
                         ld_out=7168, part_std=0.7)
     di = DevInputs(synth.generate(wl, seed=23))
-    say("split ring graph: eager")
+    say("graph T=%d: eager" % T)
     binding.check(di.call(wl))
     _sync()
     want = host(di.out)
@@ -578,7 +579,7 @@ def test_split_ring_graph_replay():
     di.reset_out()
     _sync()
     g = torch.cuda.CUDAGraph()
-    say("split ring graph: capture")
+    say("graph T=%d: capture" % T)
     with torch.cuda.graph(g, stream=s):
         status = di.call(wl, stream=torch.cuda.current_stream())
     assert status == binding.LT_OK
@@ -586,7 +587,7 @@ def test_split_ring_graph_replay():
         di.reset_out()
         _sync()
         junk = torch.randn(1 << 20, device="cuda").sum()
-        say("split ring graph: replay %d" % rep)
+        say("graph T=%d: replay %d" % (T, rep))
         g.replay()
         _sync()
         np.testing.assert_array_equal(host(di.out), want)
