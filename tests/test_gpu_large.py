@@ -67,3 +67,18 @@ def test_weight_streaming_row_stride_past_4gib():
     wl = synth.Workload("wide", T=T, L=1024, H=7168, P=1, c0=8, n=7100, ld_out=ld, part_std=0.6)
     assert binding.lt_path_for(T, wl.n) == 1
     _run_sampled(wl, list(range(T)), 7168 + 64, seed=22, what="wide decode")
+
+
+def test_pingpong_gemm_row_stride_past_4gib():
+    """The 256 x 128 ping-pong kernel (T = 1000 over 7168 columns) with a row
+    stride of about 4.2 M elements: its 32-bit in-tile offsets stay below
+    1.1 GB while token tiles from row 512 on start past 4 GiB."""
+    T, ld = 1000, 4_194_312
+    wl = synth.Workload("pp_wide", T=T, L=1024, H=7168, P=1, c0=0, n=7168, ld_out=ld,
+                        part_std=0.6)
+    assert binding.lt_path_for(T, wl.n) == 2
+    cross = -(-(1 << 32) // (2 * ld))        # first row that starts past 4 GiB
+    rng = np.random.Generator(np.random.PCG64(9))
+    rows = sorted({0, 1, 63, 64, 127, 128, cross - 1, cross, cross + 1, 895, 896, T - 1,
+                   *rng.integers(0, T, 6).tolist()})
+    _run_sampled(wl, rows, 7168 + 8, seed=24, what="ping-pong wide")
