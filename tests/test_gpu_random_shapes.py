@@ -9,7 +9,8 @@ above H (so the epilogues see every alignment), one to four partials, the
 norm on or off, and a quarter of the calls in the residual form.  Every call
 is compared with the oracle on the whole buffer: the window within
 |d| <= 3e-2 + 1.6e-2*|ref|, every other element bit for bit (for the residual
-form, both buffers).
+form, both buffers).  24 more calls are drawn inside the domain of the
+256 x 128 ping-pong GEMM kernel (aligned window, 140 .. 240 such tiles).
 """
 from __future__ import annotations
 
@@ -90,3 +91,44 @@ def test_random_shape_matches_oracle(case):
     assert_window_close(host(di.out), ref_out, c0, n, "case %d out" % i)
     assert_window_close(host(rd), ref_res, c0, n, "case %d resid" % i)
     np.testing.assert_array_equal(host(pd), prefix)
+
+
+def _pingpong_cases(count=24, seed=4242):
+    """Shapes inside the 256 x 128 ping-pong kernel's domain: an aligned
+    window (c0 and the row stride multiples of 8) with 140 .. 240 tiles of
+    256 x 128 and at least four K stages."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < count:
+        L = int(rng.integers(25, 257)) * 8                 # 200 .. 2048
+        n = int(rng.integers(1800, 7200))
+        T = int(rng.integers(300, 1700))
+        tiles = -(-n // 256) * -(-T // 128)
+        if not 140 <= tiles <= 240 or T * L * n > 8e9:
+            continue
+        c0 = 8 * int(rng.integers(0, 64))
+        H = c0 + n + int(rng.integers(0, 40))
+        ld = -(-(H + int(rng.integers(0, 24))) // 8) * 8
+        P = int(rng.integers(1, 4))
+        norm = bool(rng.random() < 0.75)
+        out.append((len(out), T, L, H, P, c0, n, ld, norm))
+    return out
+
+
+@pytest.mark.parametrize("case", _pingpong_cases(), ids=lambda c: "p%02d_T%d_L%d_H%d_P%d_c%d_n%d_ld%d_%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], "norm" if c[8] else "nonorm"))
+def test_random_pingpong_shape_matches_oracle(case):
+    import torch
+    from oracle import oracle
+
+    i, T, L, H, P, c0, n, ld, norm = case
+    wl = synth.Workload("randpp", T=T, L=L, H=H, P=P, c0=c0, n=n, ld_out=ld, part_std=0.7,
+                        norm=norm)
+    d = synth.generate(wl, seed=700 + i)
+    di = DevInputs(d)
+    say("ping-pong random case %d: T=%d L=%d H=%d P=%d c0=%d n=%d ld=%d norm=%s" % (
+        i, T, L, H, P, c0, n, ld, norm))
+    binding.check(di.call(wl))
+    torch.cuda.synchronize()
+    ref = oracle.latent_tail(d["partials"], d["norm_w"], eps32(wl), d["W"], c0, n, d["out"])
+    assert_window_close(host(di.out), ref, c0, n, "ping-pong case %d" % i)
