@@ -199,7 +199,7 @@ def under_profiler():
     return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
 
 
-def power_under_load(binding, stream, sh, sets, wpool, norm_w, seconds=2.5, samples=3):
+def power_under_load(binding, stream, sh, sets, wpool, norm_w, seconds=3.0, samples=3):
     """Socket power and per-XCD shader clocks (`amd-smi metric -p -c`) while
     the T = 8192 call (norm + GEMM, own W copy per call) runs back to back
     for a few seconds, next to the package power cap (`rocm-smi
@@ -247,7 +247,7 @@ def power_under_load(binding, stream, sh, sets, wpool, norm_w, seconds=2.5, samp
 
     th = threading.Thread(target=work)
     th.start()
-    time.sleep(0.8)
+    time.sleep(1.2)
     got = []
     for _ in range(samples):
         x = sample()
@@ -271,7 +271,7 @@ def power_under_load(binding, stream, sh, sets, wpool, norm_w, seconds=2.5, samp
             "gfx_clk_mhz_mean_over_xcds": [round(c, 1) for c in clk],
             "power_cap_w": cap,
             "workload": "T=8192 call (norm + GEMM, n=7168) back to back for about %.1f s, "
-                        "sampled %d times after 0.8 s" % (seconds, len(got))}
+                        "sampled %d times after 1.2 s" % (seconds, len(got))}
 
 
 def launch_floor(hip, stream, sh, wpool, reps=10):
