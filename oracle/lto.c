@@ -108,16 +108,22 @@ int lto_max_threads(void)
  * source; the norm's variance is not computed in bf16.
  *
  * partials: [P][T][L] bf16 bits, packed.  norm_w: [L] bf16 bits or NULL.
- * y: [T][L] bf16 bits, written.  Returns 0, or -1 on bad arguments.
+ * y: [T][L] bf16 bits, written.  Returns 0, or -1 on bad arguments or when
+ * a row's scratch cannot be allocated.
  */
 int lto_latent(const uint16_t *partials, int P, int64_t T, int64_t L,
                const uint16_t *norm_w, double eps, uint16_t *y)
 {
     if (P < 1 || T < 0 || L < 1 || (T > 0 && (!partials || !y))) return -1;
 
-#pragma omp parallel for schedule(static)
+    int nomem = 0;
+#pragma omp parallel for schedule(static) reduction(| : nomem)
     for (int64_t t = 0; t < T; ++t) {
         double *sr = (double *)malloc((size_t)L * sizeof(double));
+        if (!sr) {
+            nomem = 1;
+            continue;
+        }
         /* step 1 + R1: sum of the partials in fp64, then bf16 storage */
         for (int64_t k = 0; k < L; ++k) {
             double s = 0.0;
@@ -138,7 +144,7 @@ int lto_latent(const uint16_t *partials, int P, int64_t T, int64_t L,
         }
         free(sr);
     }
-    return 0;
+    return nomem ? -1 : 0;
 }
 
 /*
@@ -255,7 +261,8 @@ int lto_latent_tail_residual(const uint16_t *partials, int P, int64_t T, int64_t
  *
  * prefix, delta, out: [T][H]; block: [T][num_slots][H]; norm_w: [H]; all
  * bf16 bits, packed.  Every other element is left untouched.
- * Returns 0, or -1 on bad arguments.
+ * Returns 0, or -1 on bad arguments or when a row's scratch cannot be
+ * allocated.
  */
 int lto_attn_res_zero_block(uint16_t *prefix, const uint16_t *delta, int64_t T, int64_t H,
                             uint16_t *block, int64_t num_slots, int64_t block_idx,
@@ -265,9 +272,14 @@ int lto_attn_res_zero_block(uint16_t *prefix, const uint16_t *delta, int64_t T, 
     if (T == 0) return 0;
     if (!prefix || !out || (block_idx >= 0 && !block)) return -1;
 
-#pragma omp parallel for schedule(static)
+    int nomem = 0;
+#pragma omp parallel for schedule(static) reduction(| : nomem)
     for (int64_t t = 0; t < T; ++t) {
         double *p = (double *)malloc((size_t)H * sizeof(double));
+        if (!p) {
+            nomem = 1;
+            continue;
+        }
         /* the updated prefix: one rounding of the exact sum */
         for (int64_t h = 0; h < H; ++h) {
             double v = lto_bf16_to_f64(prefix[t * H + h]);
@@ -290,5 +302,5 @@ int lto_attn_res_zero_block(uint16_t *prefix, const uint16_t *delta, int64_t T, 
         }
         free(p);
     }
-    return 0;
+    return nomem ? -1 : 0;
 }
