@@ -46,7 +46,7 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
 // count is within [PP_MIN_TILES, PP_MAX_TILES] (about one round of such
 // tiles) and there are at least four K stages; gemm_pp_rows() gives the
 // tile's W rows (256), or 0 where it is not used.
-constexpr int PP_MIN_TILES = 140, PP_MAX_TILES = 240;
+constexpr int PP_MIN_TILES = 140, PP_MAX_TILES = 252;
 int gemm_pp_rows(int64_t T, int L, int n, int64_t ld_out);
 hipError_t launch_gemm_pp(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,
                           uint16_t *outn, int64_t ld_out, hipStream_t stream);

@@ -93,10 +93,10 @@ def test_random_shape_matches_oracle(case):
     np.testing.assert_array_equal(host(pd), prefix)
 
 
-def _pingpong_cases(count=24, seed=4242):
+def _pingpong_cases(count=24, seed=4242, lo=140, hi=240, first=0):
     """Shapes inside the 256 x 128 ping-pong kernel's domain: an aligned
-    window (c0 and the row stride multiples of 8) with 140 .. 240 tiles of
-    256 x 128 and at least four K stages."""
+    window (c0 and the row stride multiples of 8) with lo .. hi tiles of
+    256 x 128 (the kernel takes 140 .. 252) and at least four K stages."""
     rng = np.random.Generator(np.random.PCG64(seed))
     out = []
     while len(out) < count:
@@ -104,18 +104,18 @@ def _pingpong_cases(count=24, seed=4242):
         n = int(rng.integers(1800, 7200))
         T = int(rng.integers(300, 1700))
         tiles = -(-n // 256) * -(-T // 128)
-        if not 140 <= tiles <= 240 or T * L * n > 8e9:
+        if not lo <= tiles <= hi or T * L * n > 8e9:
             continue
         c0 = 8 * int(rng.integers(0, 64))
         H = c0 + n + int(rng.integers(0, 40))
         ld = -(-(H + int(rng.integers(0, 24))) // 8) * 8
         P = int(rng.integers(1, 4))
         norm = bool(rng.random() < 0.75)
-        out.append((len(out), T, L, H, P, c0, n, ld, norm))
+        out.append((first + len(out), T, L, H, P, c0, n, ld, norm))
     return out
 
 
-@pytest.mark.parametrize("case", _pingpong_cases(), ids=lambda c: "p%02d_T%d_L%d_H%d_P%d_c%d_n%d_ld%d_%s" % (
+@pytest.mark.parametrize("case", _pingpong_cases() + _pingpong_cases(6, 4343, 241, 252, 24), ids=lambda c: "p%02d_T%d_L%d_H%d_P%d_c%d_n%d_ld%d_%s" % (
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], "norm" if c[8] else "nonorm"))
 def test_random_pingpong_shape_matches_oracle(case):
     import torch
