@@ -1086,10 +1086,7 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
         return launch_cfg<256, 256, 4, 2, 2, 4>(y, T, L, Wn, n, outn, ld_out, res, vec16, stream);
     }
     // about one round of 256 x 128 tiles: the ping-pong kernel (k_gemm_pp.hip;
-    // n = 7168, T = 640 .. 1024: 13-20 % faster per call than the shapes below;
-    // 252 tiles, T = 1100 / 1152: 27.8 / 28.3 against 28.8 / 29.3 us; the
-    // 896-column shard at T = 8191, 256 tiles with the last column tile half
-    // full, measured no better, so the window stops at 252)
+    // n = 7168, T = 640 .. 1024: 13-20 % faster per call than the shapes below)
     if (!res && vec16 && gemm_pp_rows(T, L, n, ld_out) != 0)
         return launch_gemm_pp(y, T, L, Wn, n, outn, ld_out, stream);
     if (tiles(128, 128) > 256)

@@ -45,7 +45,10 @@ hipError_t launch_gemm(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, 
 // form; `out` 16-byte aligned with ld_out % 8 == 0).  Used where the tile
 // count is within [PP_MIN_TILES, PP_MAX_TILES] (about one round of such
 // tiles) and there are at least four K stages; gemm_pp_rows() gives the
-// tile's W rows (256), or 0 where it is not used.
+// tile's W rows (256), or 0 where it is not used.  The window's top, 252
+// tiles: T = 1100 / 1152 at n = 7168 (252 tiles) took 27.8 / 28.3 against
+// 28.8 / 29.3 us per call on the shapes below; the 896-column shard at
+// T = 8191 (256 tiles, the last column tile half full) was no better there.
 constexpr int PP_MIN_TILES = 140, PP_MAX_TILES = 252;
 int gemm_pp_rows(int64_t T, int L, int n, int64_t ld_out);
 hipError_t launch_gemm_pp(const uint16_t *y, int64_t T, int L, const uint16_t *Wn, int n,

@@ -67,3 +67,10 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monk
     assert bench.gemm_traffic_bytes() is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
     assert bench.gemm_traffic_bytes() is None
+
+
+def test_committed_traffic_figure_matches_the_gemm_sources():
+    """The HBM-traffic summary under profiles/ was taken on the GEMM sources
+    as committed; a change to them without new counters would turn the
+    benchmark's `roofline.traffic` into null."""
+    assert bench.gemm_traffic_bytes() is not None
